@@ -1,0 +1,276 @@
+"""Pins for the oracle's decode, split and merge: a hand-worked golden case,
+pure-Python brute force, torch SDPA / logsumexp in float64, closed forms,
+split-merge invariance, paging invariances, and write-then-decode against
+attention over the logical token sequence."""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla_oracle as O
+from mla_paged_decode_concat_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "tiny_decode.txt")
+
+
+def _rand_case(rng, n, H=3, R=512, P=64, scale=1.0):
+    Q = rng.standard_normal((H, R + P)) * scale
+    K = rng.standard_normal((n, R + P)) * scale
+    return Q, K
+
+
+def test_golden_hand_worked_example():
+    rows = {}
+    ks = []
+    for line in open(GOLDEN):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        tag, *vals = line.split()
+        vals = [float(v) for v in vals]
+        if tag == "k":
+            ks.append(vals)
+        else:
+            rows[tag] = vals
+    Q = np.array([rows["q"]])
+    K = np.array(ks)
+    o, lse = O.attend(Q, K, 2, 1.0)
+    assert np.allclose(o[0], rows["o"], atol=1e-15, rtol=0)
+    assert abs(lse[0] - rows["lse"][0]) < 1e-15
+    assert abs(lse[0] - math.log(4.0)) < 1e-15
+    o2, lse2 = O.merge(O.partials(Q, K, 2, 1.0, [(0, 1), (1, 2)]))
+    assert np.allclose(o2[0], rows["o"], atol=1e-15, rtol=0)
+    assert abs(lse2[0] - math.log(4.0)) < 1e-15
+
+
+def _brute(Q, K, R, sm):
+    H, n = Q.shape[0], K.shape[0]
+    o = [[0.0] * R for _ in range(H)]
+    lse = [0.0] * H
+    for h in range(H):
+        s = [sm * math.fsum(Q[h, d] * K[j, d] for d in range(K.shape[1])) for j in range(n)]
+        e = [math.exp(v) for v in s]              # no max shift: tiny scores only
+        z = math.fsum(e)
+        lse[h] = math.log(z)
+        for r in range(R):
+            o[h][r] = math.fsum(e[j] * K[j, r] for j in range(n)) / z
+    return np.array(o), np.array(lse)
+
+
+@pytest.mark.parametrize("R,P", [(512, 64), (256, 64)])
+@pytest.mark.parametrize("n", [1, 2, 5, 8])
+def test_brute_force_tiny(R, P, n):
+    rng = np.random.default_rng(100 + n + R)
+    Q, K = _rand_case(rng, n, H=3, R=R, P=P, scale=0.3)
+    sm = 1.0 / math.sqrt(192.0)
+    o, lse = O.attend(Q, K, R, sm)
+    ob, lb = _brute(Q, K, R, sm)
+    assert np.max(np.abs(o - ob)) < 1e-12
+    assert np.max(np.abs(lse - lb)) < 1e-12
+
+
+@pytest.mark.parametrize("n", [1, 17, 300])
+def test_matches_torch_sdpa_and_logsumexp_fp64(n):
+    rng = np.random.default_rng(n)
+    H, R, P = 8, 512, 64
+    Q, K = _rand_case(rng, n, H=H, R=R, P=P)
+    sm = 1.0 / math.sqrt(192.0)
+    o, lse = O.attend(Q, K, R, sm)
+    tq = torch.from_numpy(Q)[None]                      # [1, H, D]
+    tk = torch.from_numpy(K)[None, None].expand(1, H, n, R + P).contiguous()
+    tv = torch.from_numpy(K[:, :R])[None, None].expand(1, H, n, R).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(tq[:, :, None, :], tk, tv, scale=sm)[0, :, 0]
+    ref_lse = torch.logsumexp(sm * (torch.from_numpy(Q) @ torch.from_numpy(K).T), dim=1)
+    assert np.max(np.abs(o - ref.numpy())) < 1e-12
+    assert np.max(np.abs(lse - ref_lse.numpy())) < 1e-12
+
+
+def test_closed_form_single_token():
+    rng = np.random.default_rng(1)
+    Q, K = _rand_case(rng, 1, H=4)
+    sm = 0.07
+    o, lse = O.attend(Q, K, 512, sm)
+    assert np.array_equal(o, np.repeat(K[:, :512], 4, axis=0))
+    assert np.allclose(lse, sm * (Q @ K[0]), atol=1e-13, rtol=0)
+
+
+def test_closed_form_zero_query_is_mean():
+    rng = np.random.default_rng(2)
+    n = 123
+    _, K = _rand_case(rng, n, H=2)
+    Q = np.zeros((2, 576))
+    o, lse = O.attend(Q, K, 512, 0.1)
+    assert np.allclose(o, K[:, :512].mean(axis=0)[None], atol=1e-14, rtol=0)
+    assert np.allclose(lse, math.log(n), atol=1e-14, rtol=0)
+
+
+def test_closed_form_shared_rope_and_zero_nope():
+    rng = np.random.default_rng(3)
+    n, sm = 50, 0.2
+    _, K = _rand_case(rng, n, H=1)
+    kpe = rng.standard_normal(64)
+    K[:, 512:] = kpe
+    Q = np.zeros((1, 576))
+    Q[0, 512:] = rng.standard_normal(64)
+    o, lse = O.attend(Q, K, 512, sm)
+    assert np.allclose(o[0], K[:, :512].mean(axis=0), atol=1e-14, rtol=0)
+    assert abs(lse[0] - (math.log(n) + sm * float(Q[0, 512:] @ kpe))) < 1e-12
+
+
+def test_closed_form_dominant_token():
+    rng = np.random.default_rng(4)
+    n = 40
+    _, K = _rand_case(rng, n, H=1, scale=0.01)
+    Q = np.zeros((1, 576))
+    Q[0, 0] = 1.0
+    K[:, 0] = 0.0
+    K[17, 0] = 60.0                       # score 60 vs 0 for every other row
+    o, lse = O.attend(Q, K, 512, 1.0)
+    assert np.max(np.abs(o[0] - K[17, :512])) < 1e-20 + 40 * 61 * math.exp(-60)
+    assert abs(lse[0] - (60.0 + math.log1p((n - 1) * math.exp(-60)))) < 1e-13
+
+
+@pytest.mark.parametrize("n", [1, 7, 100, 1027])
+def test_split_merge_equals_unsplit(n):
+    rng = np.random.default_rng(n)
+    Q, K = _rand_case(rng, n, H=4)
+    sm = 1.0 / math.sqrt(192.0)
+    o, lse = O.attend(Q, K, 512, sm)
+    for S in [1, 2, 3, 7, 16, n]:
+        bounds = O.split_bounds(n, S)
+        assert bounds[0][0] == 0 and bounds[-1][1] == n
+        assert all(a < e for a, e in bounds)
+        assert all(bounds[i][1] == bounds[i + 1][0] for i in range(len(bounds) - 1))
+        o2, l2 = O.merge(O.partials(Q, K, 512, sm, bounds))
+        assert np.max(np.abs(o2 - o)) < 1e-12
+        assert np.max(np.abs(l2 - lse)) < 1e-12
+
+
+def test_split_bounds_drop_empty_splits():
+    # ceil(5/4) = 2 per split -> [0,2) [2,4) [4,5) and the 4th split is empty
+    assert O.split_bounds(5, 4) == [(0, 2), (2, 4), (4, 5)]
+    assert O.split_bounds(1, 16) == [(0, 1)]
+    assert O.split_bounds(0, 3) == []
+
+
+def test_num_kv_splits_rule():
+    assert O.num_kv_splits(1, 256) == 1
+    assert O.num_kv_splits(512, 256) == 1
+    assert O.num_kv_splits(513, 256) == 2
+    assert O.num_kv_splits(8192, 256) == 16
+    assert O.num_kv_splits(65536, 256) == 128
+    assert O.num_kv_splits(10 ** 7, 256) == 512
+    assert O.num_kv_splits(10 ** 7, 256, batch_invariant=True) == 1
+
+
+def test_token_permutation_and_score_shift():
+    rng = np.random.default_rng(9)
+    n, sm = 64, 0.05
+    Q, K = _rand_case(rng, n, H=3)
+    o, lse = O.attend(Q, K, 512, sm)
+    perm = rng.permutation(n)
+    o2, l2 = O.attend(Q, K[perm], 512, sm)
+    assert np.max(np.abs(o2 - o)) < 1e-12 and np.max(np.abs(l2 - lse)) < 1e-12
+    # a shared rope component shifts every score of a head by the same amount
+    u = rng.standard_normal(64)
+    K[:, 512:] = u
+    o, lse = O.attend(Q, K, 512, sm)
+    dq = np.zeros_like(Q)
+    dq[:, 512:] = rng.standard_normal((3, 64))
+    o3, l3 = O.attend(Q + dq, K, 512, sm)
+    shift = sm * (dq[:, 512:] @ u)
+    assert np.max(np.abs(o3 - o)) < 1e-12
+    assert np.max(np.abs(l3 - (lse + shift))) < 1e-12
+
+
+def test_empty_sequence_reading():
+    o, lse = O.attend(np.ones((2, 576)), np.zeros((0, 576)), 512, 1.0)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def _logical_rows(batch, b):
+    """kv_c ++ k_pe of request b's tokens in sequence order, from the inputs
+    (not the cache)."""
+    slots = batch.slot_mapping.numpy()
+    valid = np.nonzero(slots >= 0)[0]
+    start = sum(batch.seq_lens_list[:b])
+    rows = valid[start:start + batch.seq_lens_list[b]]
+    kc = W.bits(batch.kv_c)[rows]
+    kp = W.bits(batch.k_pe)[rows]
+    return kc, kp
+
+
+@pytest.mark.parametrize("index,kw", [(0, {}), (1, dict(B=4, max_len=300)), (3, dict(B=5, max_len=200)),
+                                      (4, dict(B=3, max_len=1100))])
+def test_write_then_decode_equals_attention_over_inputs(index, kw):
+    """The workload's slot map and block table agree, and the oracle's write
+    and gather are inverse: decoding the written cache equals attention over
+    the token rows taken straight from the inputs."""
+    bt = W.make_batch(index, "cpu", **kw)
+    spec = bt.spec
+    scale = float(bt.scale[0]) if bt.scale is not None else None
+    cache = O.cache_write(W.bits(bt.cache), W.bits(bt.kv_c), W.bits(bt.k_pe), bt.slot_mapping.numpy(),
+                          spec.in_dtype, spec.cache_dtype, scale)
+    sm = W.SM_SCALE
+    o, lse = O.decode(W.bits(bt.q), cache, bt.block_table.numpy(), bt.seq_lens.numpy(), sm,
+                      spec.in_dtype, spec.cache_dtype, spec.R, scale)
+    for b in range(bt.B):
+        kc, kp = _logical_rows(bt, b)
+        if spec.cache_dtype == "fp8":
+            sc = np.float32(scale)
+            kc = O.fp8_e4m3fn_decode(O.fp8_e4m3fn_encode(O.to_f32_exact(kc, spec.in_dtype) / sc)) * float(sc)
+            kp = O.fp8_e4m3fn_decode(O.fp8_e4m3fn_encode(O.to_f32_exact(kp, spec.in_dtype) / sc)) * float(sc)
+            K = np.concatenate([kc, kp], axis=1)
+        else:
+            K = np.concatenate([O.to_f64(kc, spec.in_dtype), O.to_f64(kp, spec.in_dtype)], axis=1)
+        ob, lb = O.attend(O.to_f64(W.bits(bt.q)[b], spec.in_dtype), K, spec.R, sm)
+        assert np.array_equal(ob, o[b]) and np.array_equal(lb, lse[b])
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+def test_paging_invariance_block_size_and_permutation():
+    """The same logical sequences stored with block sizes 1, 16 and 64 and
+    different physical permutations decode identically (bit for bit)."""
+    rng = np.random.default_rng(11)
+    lens = [37, 100, 64]
+    H, R, P = 4, 512, 64
+    q = rng.standard_normal((3, H, R + P)).astype(np.float32)
+    seqs = [rng.standard_normal((n, R + P)).astype(np.float32) for n in lens]
+    results = []
+    for bs, seed in [(1, 0), (16, 1), (16, 2), (64, 3)]:
+        r2 = np.random.default_rng(seed)
+        nblk = [-(-n // bs) for n in lens]
+        total = sum(nblk) + 2
+        perm = r2.permutation(total)
+        cache = np.full((total, bs, R + P), np.nan, dtype=np.float32)
+        table = np.zeros((3, max(nblk)), dtype=np.int32)
+        off = 0
+        for b, n in enumerate(lens):
+            ids = perm[off:off + nblk[b]]
+            off += nblk[b]
+            table[b, :nblk[b]] = ids
+            for j in range(n):
+                cache[ids[j // bs], j % bs] = seqs[b][j]
+        results.append(O.decode(q, cache, table, np.array(lens), 0.07, "f32", "f32", R))
+    for o, lse in results[1:]:
+        assert np.array_equal(o, results[0][0]) and np.array_equal(lse, results[0][1])
+
+
+def test_fp32_arithmetic_stays_inside_tolerance():
+    """The fp32 bar (1e-5) is attainable: the same definition evaluated in
+    float32 stays well inside it on the tiny workload's shapes."""
+    rng = np.random.default_rng(5)
+    Q, K = _rand_case(rng, 100, H=4)
+    sm = 1.0 / math.sqrt(192.0)
+    o, lse = O.attend(Q, K, 512, sm)
+    Q32, K32 = Q.astype(np.float32), K.astype(np.float32)
+    s = np.float32(sm) * (Q32 @ K32.T)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l32 = m[:, 0] + np.log(e.sum(axis=1))
+    o32 = (e / e.sum(axis=1, keepdims=True)) @ K32[:, :512]
+    assert np.max(np.abs(o32 - o)) < 1e-5 / 10
+    assert np.max(np.abs(l32 - lse)) < 1e-5 / 10
