@@ -1,0 +1,269 @@
+#!/usr/bin/env python
+"""MLA paged decode benchmark on one MI355X.
+
+Workload: DeepSeek-V3 per-GPU decode in bf16 -- B=64 requests, H=128 heads,
+every sequence 8192 tokens, kv_lora_rank 512 + rope_dim 64 (576-wide cache
+rows), block_size 64, random physical blocks, N(0,1) inputs, sm_scale
+1/sqrt(192), num_kv_splits = ceil(8192/512) = 16.
+
+One step is the whole hot path for one decode iteration: the paged cache
+write of the B new tokens (one per request) followed by the split-KV decode
+(stage 1 + stage 2).  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line.  Extra fields: per-stage times from HIP events recorded
+on the launch stream, the bulk cache-write bandwidth, the batch-invariant
+(num_kv_splits = 1) step time, and the CPU oracle's time on a bounded sample.
+"""
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode µs/step, KV-read HBM GB/s and % roofline, 1 MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+class HipEvent:
+    """A raw HIP event (timing enabled).  The library records it on the
+    stream it launches on; torch.cuda.Event cannot be used for that because
+    torch creates its event lazily on its own record()."""
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+        if HipEvent._hip is None:
+            HipEvent._hip = ctypes.CDLL("libamdhip64.so.7")
+        self.handle = ctypes.c_void_p()
+        if HipEvent._hip.hipEventCreate(ctypes.byref(self.handle)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+
+    @property
+    def cuda_event(self):
+        return self.handle.value
+
+    def ms_until(self, other) -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        rc = HipEvent._hip.hipEventElapsedTime(ctypes.byref(ms), self.handle, other.handle)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if HipEvent._hip is not None and self.handle:
+            HipEvent._hip.hipEventDestroy(self.handle)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="bound on the CPU oracle's timed work (0 = skip)")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--kernel", type=int, default=0, help="stage-1 kernel: 0 auto, 1 vector ALU, 2 MFMA")
+    ap.add_argument("--grid", type=int, default=0)
+    ap.add_argument("--heads-per-group", type=int, default=0)
+    ap.add_argument("--partition", type=int, default=0)
+    ap.add_argument("--no-invariant", action="store_true", help="skip the num_kv_splits=1 timing")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mla_paged_decode_concat_amd as M
+    from mla_paged_decode_concat_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    M.load_library()
+    spec = W.SPECS[2]
+    bt = W.make_batch(2, dev, pad_table_with_spare=False)
+    B, H, R, D = bt.B, spec.H, spec.R, spec.D
+    N = sum(bt.seq_lens_list)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    S = M.num_kv_splits(max(bt.seq_lens_list), cus)
+
+    # bulk write of the whole context (reported separately)
+    ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    bulk_ms = []
+    for _ in range(3):
+        ev_a.record()
+        M.cache_write(bt.kv_c, bt.k_pe, bt.cache, bt.slot_mapping, "auto")
+        ev_b.record()
+        torch.cuda.synchronize()
+        bulk_ms.append(ev_a.elapsed_time(ev_b))
+    bulk_bytes = N * (D * 2 + D * 2 + 8)
+    bulk_gbs = bulk_bytes / (statistics.median(bulk_ms) * 1e-3) / 1e9
+
+    # per-step inputs: the newest token of every request
+    idx = bt.last_token_rows
+    step_kv_c = bt.kv_c.index_select(0, idx).contiguous()
+    step_k_pe = bt.k_pe.index_select(0, idx).contiguous()
+    step_slots = bt.slot_mapping.index_select(0, idx).contiguous()
+    ws = torch.empty(M.decode_workspace_bytes(B, H, S, R) // 4, dtype=torch.float32, device=dev)
+    o = torch.empty((B, H, R), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    kw = dict(kernel=args.kernel, grid=args.grid, heads_per_group=args.heads_per_group, partition=args.partition)
+
+    def step(S_, evs=None):
+        M.cache_write(step_kv_c, step_k_pe, bt.cache, step_slots, "auto")
+        M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, W.SM_SCALE, S_, R, workspace=ws, o=o, lse=lse,
+                 stage_events=evs, **kw)
+
+    for _ in range(args.warmup):
+        step(S)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[HipEvent() for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(S, evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    st1 = [e[0].ms_until(e[1]) for e in evs]
+    st2 = [e[1].ms_until(e[2]) for e in evs]
+    st1_ms = statistics.mean(st1)
+    st2_ms = statistics.mean(st2)
+
+    # batch-invariant run: one split per request
+    inv_us = None
+    if not args.no_invariant:
+        ws1 = torch.empty(M.decode_workspace_bytes(B, H, 1, R) // 4, dtype=torch.float32, device=dev)
+        for _ in range(3):
+            M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, W.SM_SCALE, 1, R, workspace=ws1, o=o, lse=lse, **kw)
+        torch.cuda.synchronize()
+        ta = time.perf_counter()
+        n_inv = max(5, K // 5)
+        for _ in range(n_inv):
+            M.cache_write(step_kv_c, step_k_pe, bt.cache, step_slots, "auto")
+            M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, W.SM_SCALE, 1, R, workspace=ws1, o=o, lse=lse, **kw)
+        torch.cuda.synchronize()
+        inv_us = (time.perf_counter() - ta) * 1e6 / n_inv
+
+    if args.copy_probe_mb:
+        src = torch.empty(args.copy_probe_mb * (1 << 20) // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # algorithmic bytes and flops of one stage-1 launch
+    kv_bytes = N * D * 2
+    tab_bytes = sum(-(-n // spec.block_size) for n in bt.seq_lens_list) * 4 + B * 4
+    st1_bytes = kv_bytes + B * H * D * 2 + tab_bytes
+    flops = 2.0 * H * (D + R) * N
+    st1_s = st1_ms * 1e-3
+    achieved = st1_bytes / st1_s / 1e9
+    mfma_tflops = flops / st1_s / 1e12
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(bt, step_kv_c, step_k_pe, step_slots, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(ms_per_step * 1e3, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "DeepSeek-V3 per-GPU MLA decode, bf16: B=64, H=128, seq_len 8192 each, kv_lora_rank 512, "
+                        "rope_dim 64, block_size 64, random block table, N(0,1) inputs, sm_scale 1/sqrt(192); "
+                        "step = cache write of 64 new tokens + split-KV decode",
+            "global_batch": B,
+            "seq_len": 8192,
+            "num_heads": H,
+            "num_kv_splits": S,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode stage 1",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "kv_read_gbps": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "stage1_us": round(st1_ms * 1e3, 2),
+        "stage2_us": round(st2_ms * 1e3, 2),
+        "mfma_tflops": round(mfma_tflops, 1),
+        "mfma_frac": round(mfma_tflops / BF16_PEAK_TFLOPS, 4),
+        "hbm_floor_us": round(kv_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+        "bulk_write_gbps": round(bulk_gbs, 1),
+        "batch_invariant_us_per_step": round(inv_us, 2) if inv_us else None,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(bt, step_kv_c, step_k_pe, step_slots, seconds):
+    """The oracle as it stands, on the host: the per-step write of the B new
+    tokens plus the decode of as many requests as fit in `seconds`, scaled to
+    the full batch (µs/step)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from mla_paged_decode_concat_amd import workloads as W
+    from oracle import mla_oracle as O
+
+    spec = bt.spec
+    slots = bt.slot_mapping.cpu().numpy()
+    cache = O.cache_write(W.bits(W.nan_cache(spec, bt.num_blocks, "cpu")), W.bits(bt.kv_c), W.bits(bt.k_pe),
+                          slots, spec.in_dtype, spec.cache_dtype)
+    q = W.bits(bt.q)
+    table = bt.block_table.cpu().numpy()
+    lens = bt.seq_lens.cpu().numpy()
+    skv, skp, ssl = W.bits(step_kv_c), W.bits(step_k_pe), step_slots.cpu().numpy()
+    t0 = time.perf_counter()
+    cache = O.cache_write(cache, skv, skp, ssl, spec.in_dtype, spec.cache_dtype)
+    t_write = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    done = 0
+    for b in range(bt.B):
+        O.decode(q[b:b + 1], cache, table[b:b + 1], lens[b:b + 1], W.SM_SCALE, spec.in_dtype, spec.cache_dtype,
+                 spec.R)
+        done += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    el = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": round((t_write + el / done * bt.B) * 1e6, 1),
+        "unit": "us/step",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"oracle per-step write of {bt.B} tokens + fp64 decode of {done} of {bt.B} requests "
+                  f"(8192 tokens x 128 heads each), time scaled to {bt.B} requests; host os.cpu_count()="
+                  f"{os.cpu_count()}",
+    }
+
+
+if __name__ == "__main__":
+    main()

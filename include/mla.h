@@ -1,0 +1,223 @@
+/*
+ * mla.h — C ABI of libmla_amd.so: paged latent-KV cache write and split-KV
+ * Multi-head Latent Attention (MLA) decode for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page and section):
+ *   [ESSAY] "Triton and MLA: portable attention and multi-head latent
+ *           attention" (vLLM architecture notes, source version v0.25.1).
+ *   [DIFF]  vLLM compare view whose commit is titled "fix TP": files
+ *           csrc/cache_kernels.cu, csrc/torch_bindings.cpp,
+ *           vllm/attention/ops/triton_decode_attention.py,
+ *           vllm/attention/backends/triton_mla.py.
+ *   [API]   "vllm.v1.attention.backends.mla.triton_mla" API page,
+ *           TritonMLAMetadataBuilder._reserve_attn_logits_workspace.
+ *
+ * Conventions for every call:
+ *   - Every pointer argument is device memory owned by the caller unless the
+ *     comment says otherwise.  The library never allocates, frees or
+ *     synchronises inside these calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and the call returns without waiting.  No call reads device memory on
+ *     the host, so the calls can be captured into a HIP graph.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     negative status means nothing was launched and no output was touched.
+ *   - Device-resident values (seq_lens, block_table entries, slot_mapping) are
+ *     not validated; their preconditions are stated per call.
+ */
+#ifndef MLA_AMD_MLA_H
+#define MLA_AMD_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  MLA_FP8_E4M3 is the OCP FP8 E4M3 ("e4m3fn") format: bias 7,
+ * largest finite 448, NaN = S.1111.111, no infinities. */
+typedef enum {
+  MLA_F32 = 0,
+  MLA_BF16 = 1,
+  MLA_FP8_E4M3 = 2
+} mla_dtype_t;
+
+/* Status codes. */
+enum {
+  MLA_OK = 0,
+  MLA_ERR_ARG = -1,          /* NULL required pointer, non-positive size, bad stride */
+  MLA_ERR_UNSUPPORTED = -2,  /* shape or dtype combination outside the supported set */
+  MLA_ERR_WORKSPACE = -3,    /* workspace smaller than mla_decode_workspace_bytes() */
+  MLA_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed */
+};
+
+/* Human-readable text for a status code (static storage). */
+const char* mla_status_string(int status);
+
+/*
+ * Split count for a decode batch: one split per 512 tokens of the longest
+ * sequence, clamped to [1, 2 * num_cus]; exactly 1 when batch_invariant is
+ * non-zero, so that every request is reduced in one fixed order whatever else
+ * is in the batch.  [ESSAY: Key files (_compute_num_kv_splits); Data flow]
+ * Host-only.  Returns the split count, or MLA_ERR_ARG if max_seq_len < 0 or
+ * num_cus < 1.
+ */
+int mla_num_kv_splits(int64_t max_seq_len, int num_cus, int batch_invariant);
+
+/*
+ * Bytes of the fp32 split workspace [B, H, num_kv_splits, kv_lora_rank + 1]:
+ * per (request, head, split) the normalised partial output followed by its
+ * natural-log LSE.  [ESSAY: Data flow (attn_logits shape, the "+1" LSE slot);
+ * API: _reserve_attn_logits_workspace sizes it once at the worst case]
+ * Host-only.  Returns 0 if any argument is < 1.
+ */
+size_t mla_decode_workspace_bytes(int B, int H, int num_kv_splits, int kv_lora_rank);
+
+/*
+ * Paged latent-KV cache write ("concat and cache").
+ * [DIFF: csrc/cache_kernels.cu concat_and_cache_mla_kernel and its host
+ *  launcher; csrc/torch_bindings.cpp op schema]
+ *
+ * For each token t < num_tokens with s = slot_mapping[t] >= 0, writes
+ *   cache[s / block_size][s % block_size][0 : R)     = enc(kv_c[t][0 : R))
+ *   cache[s / block_size][s % block_size][R : R + P) = enc(k_pe[t][0 : P))
+ * Tokens with s < 0 are padding and are skipped.  num_tokens is the length of
+ * slot_mapping; kv_c/k_pe may hold more rows (padding for graph capture).
+ * enc is the identity (bit copy) when cache_dtype == in_dtype, and for
+ * cache_dtype == MLA_FP8_E4M3 it is: x / (*scale) in IEEE fp32 (correctly
+ * rounded), then round-to-nearest-even to E4M3, saturating finite values
+ * beyond +-448 to +-448, NaN -> 0x7F with the sign kept.
+ *
+ *   kv_c, kv_c_row_stride : [>= num_tokens, R] rows, stride in elements
+ *   k_pe, k_pe_row_stride : [>= num_tokens, P] rows, stride in elements
+ *   in_dtype              : MLA_F32 or MLA_BF16 (both kv_c and k_pe)
+ *   slot_mapping          : int64 [num_tokens]
+ *   cache                 : [num_blocks, block_size, R + P], element type
+ *                           cache_dtype, rows contiguous inside a block,
+ *                           block_stride elements between blocks
+ *   cache_dtype           : in_dtype, or MLA_FP8_E4M3
+ *   kv_lora_rank R, rope_dim P : (512, 64) or (256, 64)  [ESSAY: Boundaries
+ *                           and failure modes, head sizes 576 and 320]
+ *   scale                 : device fp32 scalar; required iff the cache is fp8
+ * Preconditions (device data): non-negative slots are unique and
+ * < num_blocks * block_size.  Duplicate slots race.
+ * Errors: MLA_ERR_ARG (NULL pointer, num_tokens < 0, num_blocks/block_size < 1,
+ * strides too small), MLA_ERR_UNSUPPORTED (dtype pair, (R, P)), MLA_ERR_HIP.
+ * num_tokens == 0 launches nothing and returns MLA_OK.
+ */
+int mla_cache_write(const void* kv_c, int64_t kv_c_row_stride,
+                    const void* k_pe, int64_t k_pe_row_stride, int in_dtype,
+                    const int64_t* slot_mapping, int64_t num_tokens,
+                    void* cache, int cache_dtype,
+                    int64_t num_blocks, int block_size, int64_t block_stride,
+                    int kv_lora_rank, int rope_dim,
+                    const float* scale, void* stream);
+
+/*
+ * MLA decode over the paged latent cache: all H query heads attend to one
+ * shared latent KV head (MQA form).
+ * [ESSAY: Design motivation (single KV channel, head sizes 320/576, lse
+ *  returned), Data flow (forward_mqa); DIFF: triton_decode_attention.py
+ *  _fwd_grouped_kernel_stage1 and _fwd_kernel_stage2]
+ *
+ * For request b with n = seq_lens[b] tokens, token j's row is
+ *   r_j = cache[block_table[b * block_table_stride + j / block_size]][j % block_size][:]
+ * (times *kv_scale for an fp8 cache).  Head h scores
+ *   s_hj = sm_scale * <q[b][h][0 : R + P), r_j>,
+ * and returns o[b][h][:] = sum_j softmax_j(s_h) * r_j[0 : R)  (dtype q_dtype)
+ * and lse[b][h] = ln sum_j exp(s_hj)  (fp32, natural log, includes sm_scale).
+ * n == 0 gives o = 0 and lse = -inf.
+ *
+ * Two stages run on `stream`: stage 1 writes per-split normalised partial
+ * outputs and LSEs into `workspace` ([B, H, num_kv_splits, R + 1] fp32);
+ * stage 2 merges each request's partials by their LSEs.
+ * num_kv_splits bounds the number of partials per request and sets the
+ * workspace shape.  With num_kv_splits == 1 every request is one partial,
+ * reduced in a fixed order independent of the rest of the batch (batch-
+ * invariant mode, [ESSAY: Data flow]).  With num_kv_splits > 1 the library
+ * partitions each request into at most num_kv_splits contiguous token ranges
+ * chosen to balance the whole batch across the GPU's compute units.
+ *
+ *   q, q_stride_b, q_stride_h : [B, H, R + P], strides in elements, innermost
+ *                               dimension contiguous
+ *   q_dtype                   : MLA_F32 or MLA_BF16
+ *   cache, cache_dtype        : as in mla_cache_write.  Supported pairs:
+ *                               (q F32, cache F32), (q BF16, cache BF16),
+ *                               (q BF16, cache FP8_E4M3)  [ESSAY: Boundaries
+ *                               and failure modes, fp8 cache needs a bf16 query]
+ *   block_table               : int32 [B, >= max_blocks_per_seq] with row
+ *                               stride block_table_stride
+ *   seq_lens                  : int32 [B]
+ *   kv_scale                  : device fp32 scalar, required iff fp8 cache
+ *                               (one scale for the whole row: k_scale == v_scale)
+ *   workspace                 : >= mla_decode_workspace_bytes(B, H, num_kv_splits, R)
+ *                               bytes, 4-byte aligned; contents on entry are ignored
+ *   o                         : [B, H, R] contiguous, dtype q_dtype
+ *   lse                       : [B, H] contiguous fp32
+ * Preconditions (device data): 0 <= seq_lens[b] <= max_blocks_per_seq *
+ * block_size; the first ceil(seq_lens[b] / block_size) table entries of each
+ * row lie in [0, num_blocks).
+ * Errors: MLA_ERR_ARG, MLA_ERR_UNSUPPORTED ((R, P), dtype pair),
+ * MLA_ERR_WORKSPACE (workspace_bytes too small, as the pages assert the
+ * workspace split dimension equals num_kv_splits), MLA_ERR_HIP.
+ * B == 0 launches nothing and returns MLA_OK.
+ */
+int mla_decode(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_dtype,
+               int B, int H,
+               const void* cache, int cache_dtype, int64_t num_blocks, int block_size,
+               int64_t block_stride, int kv_lora_rank, int rope_dim,
+               const int32_t* block_table, int64_t block_table_stride, int max_blocks_per_seq,
+               const int32_t* seq_lens,
+               float sm_scale, const float* kv_scale,
+               int num_kv_splits,
+               float* workspace, size_t workspace_bytes,
+               void* o, float* lse, void* stream);
+
+/*
+ * Tuning and testing controls for mla_decode_ex.  Zero-initialise and set
+ * only the fields you need; zero means "library default" for every field.
+ *   partition  : 0 = default (balanced when num_kv_splits > 1),
+ *                1 = the pages' literal partition: ceil(n / num_kv_splits)
+ *                    tokens per split, empty splits skipped
+ *                    [DIFF: triton_decode_attention.py, stage 1 split range],
+ *                2 = balanced.
+ *   kernel     : 0 = default, 1 = the generic vector-ALU stage 1,
+ *                2 = the matrix-core (MFMA) stage 1 (bf16 query only).
+ *   grid       : balanced partition only: number of token chunks the batch
+ *                is cut into (0 = derived from the compute-unit count).
+ *   heads_per_group : heads handled by one stage-1 workgroup (0 = default).
+ *   stage_events : optional hipEvent_t handles (NULL entries are skipped),
+ *                recorded on `stream` before stage 1, between stage 1 and
+ *                stage 2, and after stage 2, for timing each stage.
+ */
+typedef struct {
+  int partition;
+  int kernel;
+  int grid;
+  int heads_per_group;
+  void* stage_events[3];
+  int reserved[4];
+} mla_decode_opts_t;
+
+/* mla_decode with explicit controls (opts may be NULL = all defaults).
+ * Same arguments, results within the documented tolerance of each other for
+ * every opts value, and the same error behaviour, plus MLA_ERR_ARG for an
+ * unknown opts value and MLA_ERR_UNSUPPORTED for a kernel that cannot run the
+ * given dtype or head count.  [as mla_decode] */
+int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_dtype,
+                  int B, int H,
+                  const void* cache, int cache_dtype, int64_t num_blocks, int block_size,
+                  int64_t block_stride, int kv_lora_rank, int rope_dim,
+                  const int32_t* block_table, int64_t block_table_stride, int max_blocks_per_seq,
+                  const int32_t* seq_lens,
+                  float sm_scale, const float* kv_scale,
+                  int num_kv_splits,
+                  float* workspace, size_t workspace_bytes,
+                  void* o, float* lse, void* stream,
+                  const mla_decode_opts_t* opts);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_AMD_MLA_H */

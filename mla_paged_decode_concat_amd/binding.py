@@ -1,0 +1,171 @@
+"""Thin ctypes binding over libmla_amd.so (include/mla.h).
+
+Only argument marshalling lives here: tensor pointers, strides, dtypes and the
+current HIP stream go to the C ABI; every step of the computation runs in the
+library's kernels.  There is no CPU fallback: if the library is missing or
+fails to load, calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace too small", -4: "HIP failure"}
+
+EXPORTS = ["mla_status_string", "mla_num_kv_splits", "mla_decode_workspace_bytes", "mla_cache_write",
+           "mla_decode", "mla_decode_ex"]
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({status})")
+        self.status = status
+
+
+class DecodeOpts(ctypes.Structure):
+    _fields_ = [("partition", ctypes.c_int), ("kernel", ctypes.c_int), ("grid", ctypes.c_int),
+                ("heads_per_group", ctypes.c_int), ("stage_events", ctypes.c_void_p * 3),
+                ("reserved", ctypes.c_int * 4)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(HERE, "libmla_amd.so")
+
+
+def load_library():
+    """Load (once) and return the ctypes handle; raises if not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise FileNotFoundError(f"{path} is not built; run __graft_entry__.build() "
+                                "or python -m mla_paged_decode_concat_amd.build")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_status_string.argtypes = [i32]
+    lib.mla_num_kv_splits.restype = i32
+    lib.mla_num_kv_splits.argtypes = [i64, i32, i32]
+    lib.mla_decode_workspace_bytes.restype = sz
+    lib.mla_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.mla_cache_write.restype = i32
+    lib.mla_cache_write.argtypes = [vp, i64, vp, i64, i32, vp, i64, vp, i32, i64, i32, i64, i32, i32, vp, vp]
+    dec = [vp, i64, i64, i32, i32, i32, vp, i32, i64, i32, i64, i32, i32, vp, i64, i32, vp, f32, vp, i32,
+           vp, sz, vp, vp, vp]
+    lib.mla_decode.restype = i32
+    lib.mla_decode.argtypes = dec
+    lib.mla_decode_ex.restype = i32
+    lib.mla_decode_ex.argtypes = dec + [ctypes.POINTER(DecodeOpts)]
+    _lib = lib
+    return lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MLA_F32
+    if t.dtype == torch.bfloat16:
+        return MLA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return MLA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise MLAError(status, what)
+
+
+def num_kv_splits(max_seq_len: int, num_cus: Optional[int] = None, batch_invariant: bool = False) -> int:
+    """Split count: ceil(max_seq_len / 512) clamped to [1, 2 * CUs]; 1 when batch-invariant."""
+    if num_cus is None:
+        num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    r = load_library().mla_num_kv_splits(int(max_seq_len), int(num_cus), int(bool(batch_invariant)))
+    _check(r if r < 0 else 0, "mla_num_kv_splits")
+    return r
+
+
+def decode_workspace_bytes(B: int, H: int, num_kv_splits: int, kv_lora_rank: int) -> int:
+    return int(load_library().mla_decode_workspace_bytes(B, H, num_kv_splits, kv_lora_rank))
+
+
+def cache_write(kv_c: torch.Tensor, k_pe: torch.Tensor, kv_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                kv_cache_dtype: str = "auto", scale: Optional[torch.Tensor] = None) -> None:
+    """Scatter kv_c [T', R] and k_pe [T', P] into kv_cache [num_blocks, block_size, R+P]
+    at slot_mapping [T] (T <= T'; slot -1 = skip).  kv_cache_dtype "auto" stores
+    the input dtype; "fp8"/"fp8_e4m3" encodes with the device fp32 scalar ``scale``."""
+    in_dt = _dtype_code(kv_c)
+    cache_dt = _dtype_code(kv_cache)
+    if kv_cache_dtype.startswith("fp8") != (cache_dt == MLA_FP8_E4M3):
+        raise ValueError("kv_cache_dtype does not match the cache tensor's dtype")
+    if k_pe.dtype != kv_c.dtype or slot_mapping.dtype != torch.int64:
+        raise TypeError("k_pe must match kv_c's dtype and slot_mapping must be int64")
+    if kv_c.stride(-1) != 1 or k_pe.stride(-1) != 1 or kv_cache.stride(-1) != 1 or kv_cache.stride(1) != kv_cache.shape[2]:
+        raise ValueError("rows must be contiguous")
+    if not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be contiguous")
+    st = load_library().mla_cache_write(
+        kv_c.data_ptr(), kv_c.stride(0), k_pe.data_ptr(), k_pe.stride(0), in_dt,
+        slot_mapping.data_ptr(), slot_mapping.numel(),
+        kv_cache.data_ptr(), cache_dt, kv_cache.shape[0], kv_cache.shape[1], kv_cache.stride(0),
+        kv_c.shape[1], k_pe.shape[1],
+        scale.data_ptr() if scale is not None else None, _stream(kv_c.device))
+    _check(st, "mla_cache_write")
+
+
+def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+           sm_scale: float, num_kv_splits: int, kv_lora_rank: int = 512,
+           kv_scale: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+           partition: int = 0, kernel: int = 0, grid: int = 0, heads_per_group: int = 0,
+           stage_events=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """MLA decode of q [B, H, R+P] against the paged latent cache.  Returns
+    o [B, H, R] (q's dtype) and the natural-log lse [B, H] (fp32)."""
+    if isinstance(q, tuple):
+        q = torch.cat(q, dim=-1)
+    B, H, D = q.shape
+    R = kv_lora_rank
+    P = D - R
+    if q.stride(-1) != 1 or kv_cache.stride(-1) != 1 or kv_cache.stride(1) != kv_cache.shape[2]:
+        raise ValueError("rows must be contiguous")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise TypeError("block_table and seq_lens must be int32 (seq_lens contiguous)")
+    if block_table.stride(-1) != 1:
+        raise ValueError("block_table rows must be contiguous")
+    lib = load_library()
+    if o is None:
+        o = torch.empty((B, H, R), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    need = lib.mla_decode_workspace_bytes(max(B, 1), H, num_kv_splits, R)
+    if workspace is None:
+        workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=q.device)
+    if not (o.is_contiguous() and lse.is_contiguous() and lse.dtype == torch.float32 and o.dtype == q.dtype):
+        raise ValueError("o must be contiguous in q's dtype and lse contiguous fp32")
+    opts = DecodeOpts(partition, kernel, grid, heads_per_group)
+    if stage_events is not None:   # three torch.cuda.Event (or None) recorded around the two stages
+        for i, ev in enumerate(stage_events):
+            opts.stage_events[i] = ev.cuda_event if ev is not None else None
+    st = lib.mla_decode_ex(
+        q.data_ptr(), q.stride(0), q.stride(1), _dtype_code(q), B, H,
+        kv_cache.data_ptr(), _dtype_code(kv_cache), kv_cache.shape[0], kv_cache.shape[1], kv_cache.stride(0),
+        R, P, block_table.data_ptr(), block_table.stride(0), block_table.shape[1], seq_lens.data_ptr(),
+        float(sm_scale), kv_scale.data_ptr() if kv_scale is not None else None, int(num_kv_splits),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), o.data_ptr(), lse.data_ptr(),
+        _stream(q.device), ctypes.byref(opts))
+    _check(st, "mla_decode")
+    return o, lse

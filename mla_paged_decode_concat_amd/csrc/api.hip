@@ -1,0 +1,228 @@
+// C ABI of libmla_amd (declared in include/mla.h): argument validation,
+// split planning and kernel launches.  Nothing here reads device memory,
+// allocates, or synchronises, so every call can be captured into a HIP graph.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "mla.h"
+#include "mla_launch.h"
+
+using namespace mla;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_num_cus[kMaxDevices];   // 0 = not queried yet
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = __atomic_load_n(&g_num_cus[dev], __ATOMIC_RELAXED);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+  __atomic_store_n(&g_num_cus[dev], n, __ATOMIC_RELAXED);
+  return n;
+}
+
+bool shape_supported(int R, int P) { return (R == 512 && P == 64) || (R == 256 && P == 64); }
+
+int elem_bytes(int dt) { return dt == MLA_F32 ? 4 : dt == MLA_BF16 ? 2 : 1; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported shape or dtype combination";
+    case MLA_ERR_WORKSPACE: return "workspace too small";
+    case MLA_ERR_HIP: return "HIP runtime or launch failure";
+    default: return "unknown status";
+  }
+}
+
+int mla_num_kv_splits(int64_t max_seq_len, int num_cus, int batch_invariant) {
+  if (max_seq_len < 0 || num_cus < 1) return MLA_ERR_ARG;
+  if (batch_invariant) return 1;
+  int64_t s = (max_seq_len + 511) / 512;
+  const int64_t cap = 2 * (int64_t)num_cus;
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+size_t mla_decode_workspace_bytes(int B, int H, int num_kv_splits, int kv_lora_rank) {
+  if (B < 1 || H < 1 || num_kv_splits < 1 || kv_lora_rank < 1) return 0;
+  return (size_t)B * (size_t)H * (size_t)num_kv_splits * ((size_t)kv_lora_rank + 1) * sizeof(float);
+}
+
+int mla_cache_write(const void* kv_c, int64_t kv_c_row_stride,
+                    const void* k_pe, int64_t k_pe_row_stride, int in_dtype,
+                    const int64_t* slot_mapping, int64_t num_tokens,
+                    void* cache, int cache_dtype,
+                    int64_t num_blocks, int block_size, int64_t block_stride,
+                    int kv_lora_rank, int rope_dim,
+                    const float* scale, void* stream) {
+  if (in_dtype != MLA_F32 && in_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (cache_dtype != in_dtype && cache_dtype != MLA_FP8_E4M3) return MLA_ERR_UNSUPPORTED;
+  if (!shape_supported(kv_lora_rank, rope_dim)) return MLA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_blocks < 1 || block_size < 1) return MLA_ERR_ARG;
+  const int D = kv_lora_rank + rope_dim;
+  if (block_stride < (int64_t)block_size * D) return MLA_ERR_ARG;
+  if (kv_c_row_stride < kv_lora_rank || k_pe_row_stride < rope_dim) return MLA_ERR_ARG;
+  if ((cache_dtype == MLA_FP8_E4M3) != (scale != nullptr)) return MLA_ERR_ARG;
+  if (num_tokens == 0) return MLA_OK;
+  if (!kv_c || !k_pe || !slot_mapping || !cache) return MLA_ERR_ARG;
+
+  WriteParams p;
+  p.kv_c = kv_c;
+  p.k_pe = k_pe;
+  p.kv_c_stride = kv_c_row_stride;
+  p.k_pe_stride = k_pe_row_stride;
+  p.slots = slot_mapping;
+  p.num_tokens = num_tokens;
+  p.cache = cache;
+  p.block_stride = block_stride;
+  p.block_size = block_size;
+  p.R = kv_lora_rank;
+  p.P = rope_dim;
+  p.scale = scale;
+
+  const int ib = elem_bytes(in_dtype), cb = elem_bytes(cache_dtype);
+  const int out_vec = 16 / ib * cb;   // bytes written per 16-byte input vector
+  const bool vec = aligned16(kv_c) && aligned16(k_pe) &&
+                   (kv_c_row_stride * ib) % 16 == 0 && (k_pe_row_stride * ib) % 16 == 0 &&
+                   (reinterpret_cast<uintptr_t>(cache) % out_vec) == 0 &&
+                   (block_stride * cb) % out_vec == 0 && ((int64_t)D * cb) % out_vec == 0 &&
+                   ((int64_t)kv_lora_rank * cb) % out_vec == 0;
+  (void)hipGetLastError();
+  hipError_t e = launch_cache_write(in_dtype, cache_dtype, p, vec, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_dtype,
+                  int B, int H,
+                  const void* cache, int cache_dtype, int64_t num_blocks, int block_size,
+                  int64_t block_stride, int kv_lora_rank, int rope_dim,
+                  const int32_t* block_table, int64_t block_table_stride, int max_blocks_per_seq,
+                  const int32_t* seq_lens,
+                  float sm_scale, const float* kv_scale,
+                  int num_kv_splits,
+                  float* workspace, size_t workspace_bytes,
+                  void* o, float* lse, void* stream,
+                  const mla_decode_opts_t* opts) {
+  mla_decode_opts_t op;
+  memset(&op, 0, sizeof(op));
+  if (opts) op = *opts;
+  if (op.partition < 0 || op.partition > 2 || op.kernel < 0 || op.kernel > 2 || op.grid < 0 ||
+      op.heads_per_group < 0)
+    return MLA_ERR_ARG;
+
+  const bool pair_ok = (q_dtype == MLA_F32 && cache_dtype == MLA_F32) ||
+                       (q_dtype == MLA_BF16 && cache_dtype == MLA_BF16) ||
+                       (q_dtype == MLA_BF16 && cache_dtype == MLA_FP8_E4M3);
+  if (!pair_ok) return MLA_ERR_UNSUPPORTED;
+  if (!shape_supported(kv_lora_rank, rope_dim)) return MLA_ERR_UNSUPPORTED;
+  if (B < 0 || H < 1 || num_kv_splits < 1 || num_blocks < 1 || block_size < 1 || max_blocks_per_seq < 1)
+    return MLA_ERR_ARG;
+  const int D = kv_lora_rank + rope_dim;
+  if (block_stride < (int64_t)block_size * D || block_table_stride < max_blocks_per_seq) return MLA_ERR_ARG;
+  if (q_stride_b < 1 || q_stride_h < 1) return MLA_ERR_ARG;
+  if (!isfinite(sm_scale)) return MLA_ERR_ARG;
+  if ((cache_dtype == MLA_FP8_E4M3) != (kv_scale != nullptr)) return MLA_ERR_ARG;
+  if (B == 0) return MLA_OK;
+  if (!q || !cache || !block_table || !seq_lens || !workspace || !o || !lse) return MLA_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(workspace) % 4 != 0) return MLA_ERR_ARG;
+  if (workspace_bytes < mla_decode_workspace_bytes(B, H, num_kv_splits, kv_lora_rank)) return MLA_ERR_WORKSPACE;
+
+  // stage-1 kernel: MFMA for bf16 queries when the geometry allows it
+  const bool mfma_ok = q_dtype == MLA_BF16 && mfma_supported(H, kv_lora_rank, cache_dtype) && aligned16(q) &&
+                       (q_stride_b * 2) % 16 == 0 && (q_stride_h * 2) % 16 == 0 &&
+                       aligned16(cache) && (block_stride * elem_bytes(cache_dtype)) % 16 == 0;
+  bool use_mfma;
+  if (op.kernel == 2) {
+    if (!mfma_ok) return MLA_ERR_UNSUPPORTED;
+    use_mfma = true;
+  } else if (op.kernel == 1) {
+    use_mfma = false;
+  } else {
+    use_mfma = mfma_ok;
+  }
+
+  DecodeParams p;
+  p.q = q;
+  p.q_sb = q_stride_b;
+  p.q_sh = q_stride_h;
+  p.cache = cache;
+  p.block_stride = block_stride;
+  p.block_table = block_table;
+  p.bt_stride = block_table_stride;
+  p.seq_lens = seq_lens;
+  p.kv_scale = kv_scale;
+  p.ws = workspace;
+  p.o = o;
+  p.lse = lse;
+  p.sm_scale = sm_scale;
+  p.B = B;
+  p.H = H;
+  p.S = num_kv_splits;
+  p.block_size = block_size;
+  if (num_kv_splits == 1 || op.partition == 1) p.partition = PART_LITERAL;
+  else p.partition = PART_BALANCED;
+
+  const int cus = device_cu_count();
+  int groups;   // head groups per token chunk
+  if (use_mfma) {
+    p.heads_per_group = op.heads_per_group ? op.heads_per_group : mfma_heads_per_group(H, num_kv_splits);
+    if (!mfma_group_ok(p.heads_per_group) || H % p.heads_per_group != 0) return MLA_ERR_ARG;
+    groups = (H + p.heads_per_group - 1) / p.heads_per_group;
+  } else {
+    p.heads_per_group = 4;
+    groups = (H + 3) / 4;
+  }
+  if (op.grid) {
+    p.G = op.grid;
+  } else {
+    // one resident workgroup per compute unit for the MFMA kernel (its LDS
+    // pipeline fills the CU); the vector kernel runs four per CU
+    const int per_cu = use_mfma ? 1 : 4;
+    int g = cus * per_cu / groups;
+    p.G = g < 1 ? 1 : g;
+  }
+
+  (void)hipGetLastError();
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(op.stage_events);
+  if (ev[0] && hipEventRecord(ev[0], st) != hipSuccess) return MLA_ERR_HIP;
+  hipError_t e = use_mfma ? launch_stage1_mfma(cache_dtype, kv_lora_rank, p, st)
+                          : launch_stage1_valu(q_dtype, cache_dtype, kv_lora_rank, p, st);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  if (ev[1] && hipEventRecord(ev[1], st) != hipSuccess) return MLA_ERR_HIP;
+  e = launch_stage2(q_dtype, kv_lora_rank, p, st);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  if (ev[2] && hipEventRecord(ev[2], st) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+int mla_decode(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_dtype,
+               int B, int H,
+               const void* cache, int cache_dtype, int64_t num_blocks, int block_size,
+               int64_t block_stride, int kv_lora_rank, int rope_dim,
+               const int32_t* block_table, int64_t block_table_stride, int max_blocks_per_seq,
+               const int32_t* seq_lens,
+               float sm_scale, const float* kv_scale,
+               int num_kv_splits,
+               float* workspace, size_t workspace_bytes,
+               void* o, float* lse, void* stream) {
+  return mla_decode_ex(q, q_stride_b, q_stride_h, q_dtype, B, H, cache, cache_dtype, num_blocks, block_size,
+                       block_stride, kv_lora_rank, rope_dim, block_table, block_table_stride, max_blocks_per_seq,
+                       seq_lens, sm_scale, kv_scale, num_kv_splits, workspace, workspace_bytes, o, lse, stream,
+                       nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,500 @@
+// Split-KV MLA decode, stage 1, on the gfx950 matrix cores.
+//
+// What it computes is stage 1 of the split-KV decode of the "fix TP" vLLM
+// diff (vllm/attention/ops/triton_decode_attention.py,
+// _fwd_grouped_kernel_stage1): for one request's token range and a group of
+// heads, scores s = sm_scale * q . row over the full R+P row, an online
+// softmax, values = the first R columns of the same rows, and the stored
+// partial (acc / l, m + ln l) in the fp32 workspace [B, H, S, R+1].
+//
+// How (MI355X-first, not the pages' Triton tiling):
+//  * One workgroup owns a token range and up to 128 heads, so each 32-token
+//    KV tile is read from HBM once and shared by every head (the Triton
+//    prior art re-reads it per 16-head group).
+//  * Tiles stream HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging),
+//    STAGES tiles in flight.  Inside a tile, 16 tokens x 64 bytes form one
+//    1 KB block written by one load instruction; the slot swizzle
+//    16*q + (t ^ (12*(q & 1))) keeps both LDS read patterns below free of
+//    bank conflicts.
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: A = K rows from LDS
+//    (ds_read_b128), B = Q^T kept in registers for the whole range.
+//  * O^T = V^T P^T: A = V^T via ds_read_b64_tr_b16 (4 tokens x 1 column per
+//    lane), B = P^T taken straight from the S^T accumulators: the MFMA
+//    result layout (lane = head, 4 consecutive tokens per lane group) is the
+//    B-operand layout once the 8 k-slots of a lane are bound to tokens
+//    {4g..4g+3, 16+4g..16+4g+3}.  Every per-head quantity therefore lives in
+//    the lane that owns the head; nothing moves across lanes per tile.
+//  * Lazy rescaling: a head's running max only moves when the tile max
+//    exceeds it by more than 8 (log2 units), so exp2(s - m) <= 256 and the
+//    O rescale is rare.  acc and l always share the same reference max, so
+//    the result is the exact softmax.
+//  * The request's block-table slice is staged in LDS, so page lookups are
+//    LDS reads and never wait behind the tile loads on the vmcnt counter.
+//  * Workgroups that share a token range (different head groups) get ids
+//    that the dispatcher sends to the same XCD, so their common KV tiles
+//    meet in that XCD's L2.
+#include "mla_device.h"
+#include "mla_launch.h"
+
+namespace mla {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+#define MLA_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
+
+constexpr int kTile = 32;            // tokens per KV tile
+constexpr int kTableWindow = 1024;   // block-table entries staged in LDS
+constexpr int kXcds = 8;             // MI355X: workgroup i runs on XCD i % 8
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kSlack = 32.0f;        // log2 units: p = 2^(s - m_ref) stays below 2^32
+
+template <int R>
+struct Geo {
+  static constexpr int D = R + 64;
+  static constexpr int ROW_BYTES = D * 2;          // bf16 row
+  static constexpr int CHUNKS = ROW_BYTES / 16;    // 16-byte chunks per row
+  static constexpr int NBLK = CHUNKS / 4 * 2;      // 1 KB blocks per tile
+  static constexpr int TILE_BYTES = NBLK * 1024;
+  static constexpr int KS = D / 32;                // QK k-steps of 32
+  static constexpr int CB = R / 16;                // PV column blocks of 16
+};
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// 16 bytes per lane HBM -> LDS (global_load_lds_dwordx4): lane i's bytes land
+// at LDS address lds_base + 16 * i.  Issued through inline asm so the compiler
+// does not add a full vmcnt drain before every later LDS read (it cannot
+// prove the in-flight tile and the tile being read are disjoint); the kernel
+// orders them itself with wait_vmcnt + a workgroup barrier.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
+               "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)MLA_LDS(const char, p);
+}
+
+template <int R, int NB, int NW, int STAGES>
+struct Stage1 {
+  using G = Geo<R>;
+  static constexpr int LPW = G::NBLK / NW;         // DMA instructions per wave per tile
+  static_assert(G::NBLK % NW == 0, "tile blocks must split evenly over the waves");
+  static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
+  static constexpr int HPG = 16 * NB * NW;         // heads per workgroup
+  static constexpr int SMEM = STAGES * G::TILE_BYTES;
+
+  // wait until the loads of the tile that has `after` newer tiles in flight landed
+  static __device__ __forceinline__ void wait_tile(int after) {
+    if constexpr (STAGES >= 4) {
+      if (after >= 2) { wait_vmcnt<2 * LPW>(); return; }
+    }
+    if constexpr (STAGES >= 3) {
+      if (after >= 1) { wait_vmcnt<LPW>(); return; }
+    }
+    wait_vmcnt<0>();
+  }
+
+  static __device__ __forceinline__ void issue_tile(const DecodeParams& p, int tile_start, int se, int pg0,
+                                                    char* buf, const int* s_table, int tt_dma, int wave, int g) {
+    const char* cache = reinterpret_cast<const char*>(p.cache);
+    const char* rows[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      int tok = tile_start + 16 * tb + tt_dma;
+      tok = tok < se ? tok : se - 1;              // past the range: re-read a valid row (masked later)
+      const int pg = tok / p.block_size;
+      const long long page = s_table[pg - pg0];
+      rows[tb] = cache + (page * p.block_stride + (long long)(tok - pg * p.block_size) * G::D) * 2;
+    }
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int kb = wave + NW * i;
+      const char* src = rows[kb & 1] + (4 * (kb >> 1) + g) * 16;
+      dma16(src, lds_addr(buf) + kb * 1024);
+    }
+  }
+
+  // Token range [a, e) of request b for this wave's heads; writes partial `part`.
+  static __device__ void piece(const DecodeParams& p, int b, int a, int e, int part, int head0,
+                               char* smem, int* s_table, int* s_flags) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int r16 = lane & 15;
+
+    // ---- Q^T operand in registers: lane = head r16 of block nb, dims 32ks + 8g .. +8
+    bf16x8_t qf[NB][G::KS];
+    const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + (long long)b * p.q_sb;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int h = head0 + 16 * nb + r16;     // head groups divide H: always a real head
+#pragma unroll
+      for (int ks = 0; ks < G::KS; ++ks)
+        qf[nb][ks] = *reinterpret_cast<const bf16x8_t*>(qb + (long long)h * p.q_sh + 32 * ks + 8 * g);
+    }
+    // Q has landed before the tile loop starts: without this the compiler
+    // guards each first use of Q inside the loop with a vmcnt wait, which
+    // would also drain the tile loads in flight on every iteration.
+    wait_vmcnt<0>();
+
+    f32x4_t acc[G::CB][NB];
+    float m_ref[NB], l_sum[NB], m_init[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) m_init[nb] = -INFINITY;
+    const float c2 = p.sm_scale * kLog2e;
+
+    // lane-constant LDS offsets
+    // K rows (A operand of QK): token r16 of a 16-token block, chunk 4ks + g
+    const uint32_t k_off = (uint32_t)((16 * g + (r16 ^ (12 * (g & 1)))) * 16);
+    // V^T (A operand of PV) via transpose reads: this lane addresses token
+    // 4g + (r16 >> 2), bytes [8 * (r16 & 3), +8) of a 16-column block
+    uint32_t v_off[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int s = r16 & 3;
+      const int q = 2 * par + (s >> 1);
+      const int tt = 4 * g + (r16 >> 2);
+      v_off[par] = (uint32_t)((16 * q + (tt ^ (12 * (q & 1)))) * 16 + (s & 1) * 8);
+    }
+    // DMA role: slot `lane` of a block holds token tt_dma of its 16, chunk 4cq + g
+    const int tt_dma = r16 ^ (12 * (g & 1));
+
+    const int bs = p.block_size;
+    const int32_t* btab = p.block_table + (long long)b * p.bt_stride;
+
+    // Softmax reference: each head's running max is fixed on the first tile
+    // of the pass (the accumulators are still zero there, so nothing is
+    // rescaled) and p = 2^(s - m_ref) is accumulated unscaled after that.  A
+    // later tile more than kSlack above the reference cannot be represented;
+    // then the workgroup finishes the tile, drops the pass and redoes the
+    // range with the larger reference.  Each redo raises a reference by more
+    // than kSlack, so this terminates; on real attention scores it does not
+    // happen.  The accumulators are never multiplied, which keeps them in
+    // the accumulation registers.
+#pragma unroll 1
+    for (;;) {
+#pragma unroll
+      for (int cb = 0; cb < G::CB; ++cb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[cb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        m_ref[nb] = m_init[nb];
+        l_sum[nb] = 0.0f;
+      }
+      bool redo = false;
+
+      for (int sa = a; sa < e && !redo;) {
+        const int pg0 = sa / bs;
+        const long long win_end = (long long)(pg0 + kTableWindow) * bs;
+        int se = e;
+        if (win_end < e) se = sa + (int)((win_end - sa) / kTile) * kTile;
+        __syncthreads();   // earlier readers of s_table, s_flags and the tile buffers are done
+        const int npg = (se - 1) / bs - pg0 + 1;
+        for (int i = threadIdx.x; i < npg; i += NW * 64) s_table[i] = btab[pg0 + i];
+        if (threadIdx.x == 0) {
+          s_flags[0] = 0;
+          s_flags[1] = 0;
+        }
+        __syncthreads();
+
+        const int ntiles = (se - sa + kTile - 1) / kTile;
+#pragma unroll
+        for (int t = 0; t < STAGES - 1; ++t)
+          if (t < ntiles) issue_tile(p, sa + kTile * t, se, pg0, smem + t * G::TILE_BYTES, s_table, tt_dma, wave, g);
+
+#pragma unroll 1
+        for (int t = 0; t < ntiles; ++t) {
+          const int after = min(STAGES - 2, ntiles - 1 - t);
+          wait_tile(after);
+          __syncthreads();   // tile t landed in every wave; tile t-1's buffer is free
+          // a redo flagged while computing tile t-1 is seen by all waves here
+          if (t > 0 && s_flags[(t - 1) & 1]) {
+            redo = true;
+            break;
+          }
+          if (t + STAGES - 1 < ntiles)
+            issue_tile(p, sa + kTile * (t + STAGES - 1), se, pg0,
+                       smem + ((t + STAGES - 1) % STAGES) * G::TILE_BYTES, s_table, tt_dma, wave, g);
+          const char* tile = smem + (t % STAGES) * G::TILE_BYTES;
+          const int tile_start = sa + kTile * t;
+
+          // ---- S^T = K Q^T  (2 token blocks x NB head blocks); K rows read two
+          // k-steps ahead through a 3-slot ring, one k-step per scheduling region
+          f32x4_t s[2][NB];
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) s[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          bf16x8_t kr[3][2];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) kr[ks][mb] = *MLA_LDS(const bf16x8_t, tile + (2 * ks + mb) * 1024 + k_off);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ks = 0; ks < G::KS; ++ks) {
+            if (ks + 2 < G::KS) {
+#pragma unroll
+              for (int mb = 0; mb < 2; ++mb)
+                kr[(ks + 2) % 3][mb] = *MLA_LDS(const bf16x8_t, tile + (2 * (ks + 2) + mb) * 1024 + k_off);
+            }
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb)
+                s[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks % 3][mb], qf[nb][ks], s[mb][nb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+
+          // ---- softmax in the log2 domain; lane owns head r16, tokens 16mb + 4g + i
+          bool need = false;
+          float mt[NB];
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            mt[nb] = -INFINITY;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int tok = tile_start + 16 * mb + 4 * g + i;
+                const float v = tok < se ? s[mb][nb][i] * c2 : -INFINITY;
+                s[mb][nb][i] = v;
+                mt[nb] = fmaxf(mt[nb], v);
+              }
+            need |= mt[nb] > m_ref[nb] + kSlack;    // also true while m_ref is unset (-inf)
+          }
+          if (__builtin_expect(__any(need), 0)) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+              float m = mt[nb];
+              m = fmaxf(m, __shfl_xor(m, 16, 64));
+              m = fmaxf(m, __shfl_xor(m, 32, 64));
+              if (m_ref[nb] == -INFINITY) {
+                m_ref[nb] = m;                     // first tile of the pass
+              } else if (m > m_ref[nb] + kSlack) {
+                m_init[nb] = m;                    // not representable in this pass
+                s_flags[t & 1] = 1;
+              }
+            }
+          }
+          bf16x8_t pf[NB];
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            float ls = 0.0f;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float pj = __builtin_amdgcn_exp2f(s[mb][nb][i] - m_ref[nb]);
+                ls += pj;
+                pf[nb][4 * mb + i] = (__bf16)pj;
+              }
+            l_sum[nb] += ls;
+          }
+
+          // ---- O^T += V^T P^T  (CB column blocks x NB head blocks); V^T read
+          // two column blocks ahead through a 3-slot ring
+          auto vread = [&](int cb) -> bf16x8_t {
+            const char* vb = tile + (cb >> 1) * 2048 + v_off[cb & 1];
+            const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(MLA_LDS(bf16x4_t, vb));
+            const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(MLA_LDS(bf16x4_t, vb + 1024));
+            return bf16x8_t{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+          };
+          __builtin_amdgcn_sched_barrier(0);
+          bf16x8_t vr[3];
+          vr[0] = vread(0);
+          vr[1] = vread(1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int cb = 0; cb < G::CB; ++cb) {
+            if (cb + 2 < G::CB) vr[(cb + 2) % 3] = vread(cb + 2);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+              acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[cb % 3], pf[nb], acc[cb][nb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        if (!redo) {
+          __syncthreads();   // a redo flagged on the last tile
+          redo = s_flags[(ntiles - 1) & 1] != 0;
+        }
+        wait_vmcnt<0>();     // nothing may still be landing when the buffers are reused
+        sa = se;
+      }
+      if (!redo) break;
+    }
+
+    // ---- finalize: l over the 4 lanes sharing a head, normalise, store the partial
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float l = l_sum[nb];
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
+      const float inv = 1.0f / l;
+      const float lse = (m_ref[nb] + __builtin_amdgcn_logf(l)) * kLn2;
+      const int h = head0 + 16 * nb + r16;
+      float* dst = p.ws + (((long long)b * p.H + h) * p.S + part) * (R + 1);
+#pragma unroll
+      for (int cb = 0; cb < G::CB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[16 * cb + 4 * g + i] = acc[cb][nb][i] * inv;
+      if (g == 0) dst[R] = lse;
+    }
+  }
+};
+
+// Workgroup id -> (work item, head group): the head groups of one item get
+// ids id, id+8, id+16, ... (same XCD, dispatched together).
+__device__ __forceinline__ bool map_block(int id, int items, int groups, int& item, int& hg) {
+  const int x = id % kXcds;
+  const int j = id / kXcds;
+  hg = j % groups;
+  item = x + kXcds * (j / groups);
+  return item < items;
+}
+
+__host__ __device__ inline int mapped_grid(int items, int groups) {
+  return ((items + kXcds - 1) / kXcds) * kXcds * groups;
+}
+
+template <int R, int NB, int NW, int STAGES>
+__global__ __launch_bounds__(NW * 64) void stage1_mfma_kernel(DecodeParams p) {
+  using K = Stage1<R, NB, NW, STAGES>;
+  __shared__ __attribute__((aligned(1024))) char smem[K::SMEM];
+  __shared__ int s_table[kTableWindow];
+  __shared__ int s_flags[2];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int groups = p.H / K::HPG;
+
+  // Enumerate this workgroup's pieces (request, token range, partial index)
+  // and run each; piece() is inlined at one call site only.
+  const bool literal = p.partition == PART_LITERAL;
+  int item, hg;
+  if (!map_block(blockIdx.x, literal ? p.B * p.S : p.G, groups, item, hg)) return;
+  const int head0 = hg * K::HPG + wave * 16 * NB;
+  long long Q = 0, lo = 0, hi = 0, carry = 0;
+  int base = 0;
+  unsigned long long mask = 0;
+  long long start = 0, incl = 0;
+  int nlane = 0;
+  bool done = false;
+  if (literal) {
+    lo = item;   // the single (request, split) of this workgroup
+  } else {
+    const BatchTotals t = batch_totals(p.seq_lens, p.B, lane);
+    Q = balanced_chunk(t, p.G, p.S);
+    lo = (long long)item * Q;
+    hi = min(lo + Q, t.total);
+    done = lo >= hi;
+    base = -kWave;
+  }
+  while (!done) {
+    int b, a, e, part;
+    if (literal) {
+      done = true;
+      b = item / p.S;
+      part = item - b * p.S;
+      const int n = p.seq_lens[b];
+      const int kps = (n + p.S - 1) / p.S;
+      a = part * kps;
+      e = min(a + kps, n);
+      if (n <= 0 || e <= a) break;
+    } else {
+      while (mask == 0) {
+        if (base >= 0) carry += __shfl(incl, kWave - 1, kWave);
+        base += kWave;
+        if (base >= p.B || carry >= hi) break;
+        const int bb = base + lane;
+        nlane = bb < p.B ? max(p.seq_lens[bb], 0) : 0;
+        const long long n32 = pad32(nlane);
+        incl = wave_scan_i64(n32, lane);
+        start = carry + incl - n32;
+        mask = __ballot(nlane > 0 && start < hi && start + nlane > lo);
+      }
+      if (mask == 0) break;
+      const int j = __ffsll((long long)mask) - 1;
+      mask &= mask - 1;
+      const long long st = __shfl(start, j, kWave);
+      const int nn = __shfl(nlane, j, kWave);
+      b = base + j;
+      a = (int)(lo > st ? lo - st : 0);
+      e = (int)min(hi - st, (long long)nn);
+      part = (int)(item - st / Q);
+    }
+    // the piece is the same for every lane: say so, so that its bounds and
+    // loop counters live in scalar registers
+    K::piece(p, __builtin_amdgcn_readfirstlane(b), __builtin_amdgcn_readfirstlane(a),
+             __builtin_amdgcn_readfirstlane(e), __builtin_amdgcn_readfirstlane(part),
+             __builtin_amdgcn_readfirstlane(head0), smem, s_table, s_flags);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+bool mfma_supported(int H, int R, int cache_dtype) {
+  return cache_dtype == DT_BF16 && (R == 512 || R == 256) && H % 16 == 0;
+}
+
+bool mfma_group_ok(int hpg) { return hpg == 16 || hpg == 32 || hpg == 64 || hpg == 128; }
+
+// Heads per workgroup.  With one partial per request (num_kv_splits == 1)
+// there are only B token ranges, so the heads are spread over more
+// workgroups (their shared tiles meet in L2); otherwise one workgroup takes
+// up to 128 heads and reads each tile once.
+int mfma_heads_per_group(int H, int S) {
+  if (S == 1 && H % 32 == 0) return 32;
+  if (H % 128 == 0) return 128;
+  if (H % 64 == 0) return 64;
+  if (H % 32 == 0) return 32;
+  return 16;
+}
+
+// deepest pipeline whose wait count fits the 6-bit vmcnt field
+template <int R, int NW>
+constexpr int stages_for() {
+  return (2 * (Geo<R>::NBLK / NW) < 64) ? 4 : 3;
+}
+
+template <int R, int NB, int NW>
+static hipError_t launch_cfg(const DecodeParams& p, hipStream_t stream) {
+  constexpr int STAGES = stages_for<R, NW>();
+  using K = Stage1<R, NB, NW, STAGES>;
+  const int groups = (p.H + K::HPG - 1) / K::HPG;
+  const int items = p.partition == PART_LITERAL ? p.B * p.S : p.G;
+  dim3 grid((unsigned)mapped_grid(items, groups)), block(NW * 64);
+  hipLaunchKernelGGL((stage1_mfma_kernel<R, NB, NW, STAGES>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int R>
+static hipError_t launch_r(const DecodeParams& p, hipStream_t stream) {
+  switch (p.heads_per_group) {
+    case 128: return launch_cfg<R, 2, 4>(p, stream);
+    case 64: return launch_cfg<R, 2, 2>(p, stream);
+    case 32: return launch_cfg<R, 2, 1>(p, stream);
+    case 16: return launch_cfg<R, 1, 1>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_stage1_mfma(int cache_dtype, int R, const DecodeParams& p, hipStream_t stream) {
+  if (cache_dtype != DT_BF16) return hipErrorNotSupported;
+  return R == 512 ? launch_r<512>(p, stream) : launch_r<256>(p, stream);
+}
+
+}  // namespace mla

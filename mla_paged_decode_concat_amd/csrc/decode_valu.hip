@@ -1,0 +1,266 @@
+// Split-KV MLA decode, stage 1, vector-ALU version: the generic path for any
+// head count and the fp32 path.  Per (partial, group of 4 heads) it computes
+// the softmax-normalised partial output and the partial LSE of the heads
+// against the partial's token rows, as stage 1 of the split-KV decode does in
+// the "fix TP" vLLM diff (vllm/attention/ops/triton_decode_attention.py,
+// _fwd_grouped_kernel_stage1): scores over the full R + P row, values = the
+// first R columns of the same row, online softmax, store acc / l and m + ln l.
+//
+// Layout: 4 waves per workgroup; wave w takes every 4th token of the partial.
+// A lane holds columns lane + 64 j of the current row, so each row read is
+// coalesced; per-token dot products are finished with a wave butterfly.  The
+// four waves' (max, sum, acc) are merged through LDS at the end.
+#include "mla_device.h"
+#include "mla_launch.h"
+
+namespace mla {
+
+constexpr int kValuWaves = 4;
+constexpr int kValuHeads = 4;   // heads per workgroup
+
+template <int CT>
+__device__ __forceinline__ float load_cache_elem(const void* base, long long idx) {
+  if constexpr (CT == DT_F32) return reinterpret_cast<const float*>(base)[idx];
+  else if constexpr (CT == DT_BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+  else return fp8_to_f32(reinterpret_cast<const uint8_t*>(base)[idx]);
+}
+
+template <int QT>
+__device__ __forceinline__ float load_q_elem(const void* base, long long idx) {
+  if constexpr (QT == DT_F32) return reinterpret_cast<const float*>(base)[idx];
+  else return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+}
+
+template <int QT, int CT, int R, int P>
+__device__ void valu_piece(const DecodeParams& p, int b, int h0, int a, int e, int part,
+                           float (*sm_acc)[kValuHeads][R], float (*sm_ml)[kValuHeads][2]) {
+  constexpr int D = R + P;
+  constexpr int DJ = D / kWave;
+  constexpr int RJ = R / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+
+  // fp8: scores use code values; fold the per-tensor scale into the score
+  // scale and the output (k_scale == v_scale).
+  const float kvs = (CT == DT_FP8) ? *p.kv_scale : 1.0f;
+  const float sscale = p.sm_scale * kvs;
+
+  float qr[kValuHeads][DJ];
+#pragma unroll
+  for (int hh = 0; hh < kValuHeads; ++hh) {
+    const int h = h0 + hh;
+#pragma unroll
+    for (int j = 0; j < DJ; ++j)
+      qr[hh][j] = h < p.H ? load_q_elem<QT>(p.q, b * p.q_sb + h * p.q_sh + lane + kWave * j) : 0.0f;
+  }
+  float m[kValuHeads], l[kValuHeads], acc[kValuHeads][RJ];
+#pragma unroll
+  for (int hh = 0; hh < kValuHeads; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) acc[hh][j] = 0.0f;
+  }
+
+  const int32_t* bt = p.block_table + b * p.bt_stride;
+#pragma unroll 1
+  for (int n = a + wave; n < e; n += kValuWaves) {
+    const long long blk = bt[n / p.block_size];
+    const long long row = blk * p.block_stride + (long long)(n % p.block_size) * D;
+    float kv[DJ];
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) kv[j] = load_cache_elem<CT>(p.cache, row + lane + kWave * j);
+#pragma unroll
+    for (int hh = 0; hh < kValuHeads; ++hh) {
+      float d = 0.0f;
+#pragma unroll
+      for (int j = 0; j < DJ; ++j) d = fmaf(qr[hh][j], kv[j], d);
+      const float s = wave_sum(d) * sscale;
+      const float mn = fmaxf(m[hh], s);
+      const float alpha = expf(m[hh] - mn);
+      const float pe = expf(s - mn);
+      l[hh] = l[hh] * alpha + pe;
+#pragma unroll
+      for (int j = 0; j < RJ; ++j) acc[hh][j] = acc[hh][j] * alpha + pe * kv[j];
+      m[hh] = mn;
+    }
+  }
+
+  // merge the waves through LDS
+#pragma unroll
+  for (int hh = 0; hh < kValuHeads; ++hh) {
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) sm_acc[wave][hh][lane + kWave * j] = acc[hh][j];
+    if (lane == 0) {
+      sm_ml[wave][hh][0] = m[hh];
+      sm_ml[wave][hh][1] = l[hh];
+    }
+  }
+  __syncthreads();
+  const int S = p.S;
+  for (int idx = threadIdx.x; idx < kValuHeads * R; idx += kWave * kValuWaves) {
+    const int hh = idx / R;
+    const int d = idx - hh * R;
+    const int h = h0 + hh;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kValuWaves; ++w) M = fmaxf(M, sm_ml[w][hh][0]);
+    float L = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kValuWaves; ++w) {
+      const float mw = sm_ml[w][hh][0];
+      if (mw == -INFINITY) continue;       // this wave saw no token
+      const float c = expf(mw - M);
+      L += sm_ml[w][hh][1] * c;
+      o += sm_acc[w][hh][d] * c;
+    }
+    if (h < p.H) {
+      float* dst = p.ws + (((long long)b * p.H + h) * S + part) * (R + 1);
+      dst[d] = o / L * kvs;
+      if (d == 0) dst[R] = M + logf(L);
+    }
+  }
+  __syncthreads();   // LDS is reused by the next piece
+}
+
+template <int QT, int CT, int R, int P>
+__global__ __launch_bounds__(kWave * kValuWaves) void stage1_valu_kernel(DecodeParams p) {
+  __shared__ float sm_acc[kValuWaves][kValuHeads][R];
+  __shared__ float sm_ml[kValuWaves][kValuHeads][2];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int h0 = blockIdx.y * kValuHeads;
+
+  if (p.partition == PART_LITERAL) {
+    const int b = blockIdx.x / p.S;
+    const int s = blockIdx.x - b * p.S;
+    const int n = p.seq_lens[b];
+    if (n <= 0) return;
+    const int kps = (n + p.S - 1) / p.S;
+    const int a = s * kps;
+    const int e = min(a + kps, n);
+    if (e <= a) return;
+    valu_piece<QT, CT, R, P>(p, b, h0, a, e, s, sm_acc, sm_ml);
+    return;
+  }
+
+  // balanced: workgroup blockIdx.x owns chunk [g*Q, (g+1)*Q) of the padded line
+  const int g = blockIdx.x;
+  const BatchTotals t = batch_totals(p.seq_lens, p.B, lane);
+  const long long Q = balanced_chunk(t, p.G, p.S);
+  const long long lo = (long long)g * Q;
+  const long long hi = min(lo + Q, t.total);
+  if (lo >= hi) return;
+  long long carry = 0;
+  for (int base = 0; base < p.B; base += kWave) {
+    const int b = base + lane;
+    const int n = b < p.B ? max(p.seq_lens[b], 0) : 0;
+    const long long n32 = pad32(n);
+    const long long incl = wave_scan_i64(n32, lane);
+    const long long start = carry + incl - n32;
+    const bool ov = n > 0 && start < hi && start + n > lo;
+    unsigned long long mask = __ballot(ov);
+    while (mask) {
+      const int j = __ffsll((long long)mask) - 1;
+      mask &= mask - 1;
+      const long long st = __shfl(start, j, kWave);
+      const int nn = __shfl(n, j, kWave);
+      const int a = (int)(lo > st ? lo - st : 0);
+      const int e = (int)min(hi - st, (long long)nn);
+      const int part = (int)(g - st / Q);
+      valu_piece<QT, CT, R, P>(p, base + j, h0, a, e, part, sm_acc, sm_ml);
+    }
+    carry += __shfl(incl, kWave - 1, kWave);
+    if (carry >= hi) break;
+  }
+}
+
+template <int QT, int CT>
+static hipError_t launch_valu_t(const DecodeParams& p, int R, hipStream_t stream) {
+  dim3 block(kWave * kValuWaves);
+  const unsigned gx = p.partition == PART_LITERAL ? (unsigned)(p.B * p.S) : (unsigned)p.G;
+  dim3 grid(gx, (unsigned)((p.H + kValuHeads - 1) / kValuHeads));
+  if (R == 512) hipLaunchKernelGGL((stage1_valu_kernel<QT, CT, 512, 64>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((stage1_valu_kernel<QT, CT, 256, 64>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage1_valu(int q_dtype, int cache_dtype, int R, const DecodeParams& p, hipStream_t stream) {
+  if (q_dtype == DT_F32 && cache_dtype == DT_F32) return launch_valu_t<DT_F32, DT_F32>(p, R, stream);
+  if (q_dtype == DT_BF16 && cache_dtype == DT_BF16) return launch_valu_t<DT_BF16, DT_BF16>(p, R, stream);
+  if (q_dtype == DT_BF16 && cache_dtype == DT_FP8) return launch_valu_t<DT_BF16, DT_FP8>(p, R, stream);
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Stage 2: merge each (request, head)'s partials by their LSEs
+// ("fix TP" diff, _fwd_kernel_stage2; the merged LSE is returned as well, as
+// forward_mqa in the Triton-MLA essay returns (o, lse)).
+// One wave per (request, head); 4 heads per workgroup.
+// ---------------------------------------------------------------------------
+
+constexpr int kMergeWaves = 4;
+
+template <int QT, int R>
+__global__ __launch_bounds__(kWave * kMergeWaves) void stage2_merge_kernel(DecodeParams p) {
+  constexpr int RJ = R / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int hblocks = (p.H + kMergeWaves - 1) / kMergeWaves;
+  const int b = blockIdx.x / hblocks;
+  const int h = (blockIdx.x - b * hblocks) * kMergeWaves + wave;
+  if (h >= p.H) return;
+  const int n = p.seq_lens[b];
+  int k;
+  if (p.partition == PART_LITERAL) {
+    k = literal_num_partials(n, p.S);
+  } else {
+    const BatchTotals t = batch_totals(p.seq_lens, p.B, lane);
+    const long long Q = balanced_chunk(t, p.G, p.S);
+    k = balanced_num_partials(balanced_start(p.seq_lens, b, lane), n, Q);
+  }
+  const long long bh = (long long)b * p.H + h;
+  const float* src = p.ws + bh * p.S * (R + 1);
+  float acc[RJ];
+#pragma unroll
+  for (int j = 0; j < RJ; ++j) acc[j] = 0.0f;
+  float M = -INFINITY, L = 0.0f;
+  if (k > 0) {
+    for (int s = lane; s < k; s += kWave) M = fmaxf(M, src[(long long)s * (R + 1) + R]);
+    M = wave_max(M);
+    float Ls = 0.0f;
+    for (int s = lane; s < k; s += kWave) Ls += expf(src[(long long)s * (R + 1) + R] - M);
+    L = wave_sum(Ls);
+#pragma unroll 1
+    for (int s = 0; s < k; ++s) {
+      const float* row = src + (long long)s * (R + 1);
+      const float w = expf(row[R] - M);
+#pragma unroll
+      for (int j = 0; j < RJ; ++j) acc[j] = fmaf(w, row[lane + kWave * j], acc[j]);
+    }
+    const float inv = 1.0f / L;
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) acc[j] *= inv;
+  }
+#pragma unroll
+  for (int j = 0; j < RJ; ++j) {
+    const long long idx = bh * R + lane + kWave * j;
+    if constexpr (QT == DT_F32) reinterpret_cast<float*>(p.o)[idx] = acc[j];
+    else reinterpret_cast<uint16_t*>(p.o)[idx] = (uint16_t)f32_to_bf16_rne(acc[j]);
+  }
+  if (lane == 0) p.lse[bh] = k > 0 ? M + logf(L) : -INFINITY;
+}
+
+hipError_t launch_stage2(int q_dtype, int R, const DecodeParams& p, hipStream_t stream) {
+  const int hblocks = (p.H + kMergeWaves - 1) / kMergeWaves;
+  dim3 grid((unsigned)(p.B * hblocks)), block(kWave * kMergeWaves);
+  if (q_dtype == DT_F32) {
+    if (R == 512) hipLaunchKernelGGL((stage2_merge_kernel<DT_F32, 512>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((stage2_merge_kernel<DT_F32, 256>), grid, block, 0, stream, p);
+  } else {
+    if (R == 512) hipLaunchKernelGGL((stage2_merge_kernel<DT_BF16, 512>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((stage2_merge_kernel<DT_BF16, 256>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,194 @@
+// Internal device helpers for libmla_amd: element formats, wave reductions,
+// and the split partition shared by decode stage 1 and stage 2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Element formats
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// float -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// E4M3 ("e4m3fn") code -> float, exact.  Exponent bias 7; exponent field 0 is
+// subnormal (m * 2^-9); S.1111.111 is NaN.  Normal codes map to binary32 by
+// re-biasing the exponent (7 -> 127) and left-aligning the 3 mantissa bits.
+__device__ __forceinline__ float fp8_to_f32(uint32_t c) {
+  const uint32_t s = (c & 0x80u) << 24;
+  const uint32_t e = (c >> 3) & 0xfu;
+  const uint32_t m = c & 0x7u;
+  if (e == 0) return __uint_as_float(s | __float_as_uint((float)m * 0.001953125f));
+  if (e == 0xfu && m == 0x7u) return __uint_as_float(s | 0x7fc00000u);
+  return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
+}
+
+// float -> E4M3 code: round to nearest, ties to even; finite magnitudes
+// >= 448 and infinities saturate to +-448 (0x7E); NaN -> 0x7F; sign kept.
+// Below 2^-6 the codes are the integers round(|v| * 2^9) (subnormals, plus
+// the carry into the smallest normal, whose code 0x08 follows 0x07).  From
+// 2^-6 up the code is the binary32 exponent/top-3-mantissa field rounded at
+// bit 20 and re-biased from 127 to 7 (120 << 3 = 960).
+__device__ __forceinline__ uint32_t f32_to_fp8(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t s = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return s | 0x7fu;            // NaN
+  if (a >= 0x43e00000u) return s | 0x7eu;           // >= 448 (and inf)
+  if (a < 0x3c800000u) {                            // < 2^-6
+    const float t = __uint_as_float(a) * 512.0f;    // exact scaling by 2^9
+    return s | (uint32_t)__builtin_rintf(t);        // rint: ties to even
+  }
+  const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+  return s | ((r >> 20) - 960u);
+}
+
+// ---------------------------------------------------------------------------
+// Wave-wide reductions (64 lanes, butterfly: every lane gets the result)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ long long wave_sum_i64(long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int wave_max_i32(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// inclusive prefix sum across the wave
+__device__ __forceinline__ long long wave_scan_i64(long long v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    long long t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Split partition.
+//
+// LITERAL: the pages' rule.  Request b with n tokens is cut into splits of
+//   kps = ceil(n / S) tokens; split s covers [s*kps, min((s+1)*kps, n)) and
+//   empty splits are skipped, so the non-empty ones are s = 0..ceil(n/kps)-1.
+//
+// BALANCED: the requests, each padded to a multiple of 32 tokens, are laid
+//   end to end; that line is cut into G chunks of Q tokens (Q a multiple of
+//   32), and chunk g is handled by stage-1 workgroup g.  A request's partial
+//   p is the part of it inside chunk (first_chunk(b) + p).  Q is at least
+//   ceil(n32_max / (S - 1)), which keeps every request within S partials
+//   (a request of n32 tokens touches at most floor((n32 - 1) / Q) + 2 chunks).
+// ---------------------------------------------------------------------------
+
+enum : int { PART_LITERAL = 1, PART_BALANCED = 2 };
+
+constexpr int kChunkAlign = 32;
+
+__device__ __forceinline__ long long pad32(long long n) { return (n + 31) & ~31LL; }
+
+struct BatchTotals {
+  long long total;   // sum of padded lengths
+  int n32_max;       // longest padded length
+};
+
+// Every lane of the calling wave gets the totals.
+__device__ __forceinline__ BatchTotals batch_totals(const int32_t* __restrict__ seq_lens, int B, int lane) {
+  long long tot = 0;
+  int mx = 0;
+  for (int b = lane; b < B; b += kWave) {
+    const int n = max(seq_lens[b], 0);
+    const long long p = pad32(n);
+    tot += p;
+    mx = max(mx, (int)p);
+  }
+  BatchTotals t;
+  t.total = wave_sum_i64(tot);
+  t.n32_max = wave_max_i32(mx);
+  return t;
+}
+
+__device__ __forceinline__ long long balanced_chunk(const BatchTotals& t, int G, int S) {
+  long long q = (t.total + G - 1) / G;
+  long long qmin = S > 1 ? ((long long)t.n32_max + S - 2) / (S - 1) : (long long)t.n32_max;
+  q = q > qmin ? q : qmin;
+  q = pad32(q);
+  return q > 0 ? q : kChunkAlign;
+}
+
+// Number of partials stage 1 wrote for a request of n tokens whose padded
+// start on the balanced line is `start`.
+__device__ __forceinline__ int balanced_num_partials(long long start, int n, long long Q) {
+  if (n <= 0) return 0;
+  return (int)((start + n - 1) / Q - start / Q + 1);
+}
+
+__device__ __forceinline__ int literal_num_partials(int n, int S) {
+  if (n <= 0) return 0;
+  const int kps = (n + S - 1) / S;
+  return (n + kps - 1) / kps;
+}
+
+// Padded start of request b on the balanced line (every lane gets it).
+__device__ __forceinline__ long long balanced_start(const int32_t* __restrict__ seq_lens, int b, int lane) {
+  long long s = 0;
+  for (int i = lane; i < b; i += kWave) s += pad32(max(seq_lens[i], 0));
+  return wave_sum_i64(s);
+}
+
+// ---------------------------------------------------------------------------
+// Parameters shared by the decode kernels (passed by value).
+// ---------------------------------------------------------------------------
+
+struct DecodeParams {
+  const void* q;
+  long long q_sb, q_sh;            // elements
+  const void* cache;
+  long long block_stride;          // elements
+  const int32_t* block_table;
+  long long bt_stride;
+  const int32_t* seq_lens;
+  const float* kv_scale;           // device scalar (fp8 cache) or null
+  float* ws;                       // [B, H, S, R + 1]
+  void* o;                         // [B, H, R]
+  float* lse;                      // [B, H]
+  float sm_scale;
+  int B, H, S;
+  int block_size;
+  int partition;                   // PART_LITERAL | PART_BALANCED
+  int G;                           // balanced: chunk count
+  int heads_per_group;             // stage 1: heads per workgroup
+};
+
+}  // namespace mla

@@ -1,0 +1,35 @@
+// Host-side launchers shared between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_device.h"
+
+namespace mla {
+
+struct WriteParams {
+  const void* kv_c;
+  const void* k_pe;
+  long long kv_c_stride, k_pe_stride;   // elements
+  const int64_t* slots;
+  long long num_tokens;
+  void* cache;
+  long long block_stride;               // elements
+  int block_size;
+  int R, P;
+  const float* scale;
+};
+
+hipError_t launch_cache_write(int in_dtype, int cache_dtype, const WriteParams& p, bool vec, hipStream_t stream);
+
+hipError_t launch_stage1_valu(int q_dtype, int cache_dtype, int R, const DecodeParams& p, hipStream_t stream);
+hipError_t launch_stage1_mfma(int cache_dtype, int R, const DecodeParams& p, hipStream_t stream);
+hipError_t launch_stage2(int q_dtype, int R, const DecodeParams& p, hipStream_t stream);
+
+// Stage-1 MFMA kernel geometry, needed by the host planner.
+int mfma_heads_per_group(int H, int S);
+bool mfma_group_ok(int heads_per_group);
+bool mfma_supported(int H, int R, int cache_dtype);
+
+}  // namespace mla

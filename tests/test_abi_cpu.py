@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/mla.h declares, the host-only calls compute the documented values,
+and invalid arguments are rejected before anything is launched (no compute
+call reaches a kernel here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_paged_decode_concat_amd import binding
+from oracle import mla_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(binding.library_path()),
+                                reason="libmla_amd.so not built (run __graft_entry__.build())")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_functions_are_exported():
+    lib = binding.load_library()
+    names = _declared_functions()
+    assert set(binding.EXPORTS) <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = binding.load_library()
+    for code in [0, -1, -2, -3, -4]:
+        assert lib.mla_status_string(code)
+    assert lib.mla_status_string(12345) == b"unknown status"
+
+
+@pytest.mark.parametrize("max_len,cus,bi", [(0, 256, 0), (1, 256, 0), (512, 256, 0), (513, 256, 0), (8192, 256, 0),
+                                            (65536, 256, 0), (10 ** 8, 256, 0), (4096, 8, 0), (8192, 256, 1)])
+def test_num_kv_splits_matches_oracle(max_len, cus, bi):
+    lib = binding.load_library()
+    assert lib.mla_num_kv_splits(max_len, cus, bi) == O.num_kv_splits(max_len, cus, bool(bi))
+
+
+def test_num_kv_splits_rejects_bad_args():
+    lib = binding.load_library()
+    assert lib.mla_num_kv_splits(-1, 256, 0) == -1
+    assert lib.mla_num_kv_splits(10, 0, 0) == -1
+
+
+def test_workspace_bytes():
+    lib = binding.load_library()
+    for B, H, S, R in [(64, 128, 16, 512), (2, 4, 2, 512), (128, 32, 64, 256), (1, 1, 1, 1)]:
+        assert lib.mla_decode_workspace_bytes(B, H, S, R) == 4 * O.workspace_floats(B, H, S, R)
+    assert lib.mla_decode_workspace_bytes(0, 1, 1, 512) == 0
+    assert lib.mla_decode_workspace_bytes(1, 1, 0, 512) == 0
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _write(**kw):
+    a = dict(kv_c=FAKE, kvs=512, k_pe=FAKE, kps=64, in_dt=1, slots=FAKE, T=10, cache=FAKE, cache_dt=1,
+             nb=4, bs=16, bstride=16 * 576, R=512, P=64, scale=None, stream=None)
+    a.update(kw)
+    return binding.load_library().mla_cache_write(*a.values())
+
+
+def test_cache_write_validation():
+    assert _write(in_dt=2) == -2                    # fp8 input is not an input dtype
+    assert _write(cache_dt=0) == -2                 # bf16 in, f32 cache
+    assert _write(R=128) == -2 and _write(P=32) == -2
+    assert _write(T=-1) == -1
+    assert _write(nb=0) == -1 and _write(bs=0) == -1
+    assert _write(bstride=16 * 576 - 1) == -1
+    assert _write(kvs=511) == -1 and _write(kps=63) == -1
+    assert _write(cache_dt=2) == -1                 # fp8 cache without a scale
+    assert _write(scale=FAKE) == -1                 # scale given for a bf16 cache
+    assert _write(kv_c=None) == -1 and _write(slots=None) == -1 and _write(cache=None) == -1
+    assert _write(T=0) == 0                         # nothing to do, nothing launched
+
+
+def _decode(opts=None, **kw):
+    a = dict(q=FAKE, qsb=128 * 576, qsh=576, q_dt=1, B=4, H=128, cache=FAKE, cache_dt=1, nb=100, bs=64,
+             bstride=64 * 576, R=512, P=64, bt=FAKE, bts=10, maxblk=10, seq=FAKE, sm=0.07, kvs=None, S=4,
+             ws=FAKE, wsb=4 * 128 * 4 * 513 * 4, o=FAKE, lse=FAKE, stream=None)
+    a.update(kw)
+    lib = binding.load_library()
+    if opts is None:
+        return lib.mla_decode(*a.values())
+    return lib.mla_decode_ex(*a.values(), ctypes.byref(opts))
+
+
+def test_decode_validation():
+    assert _decode(q_dt=0) == -2                    # f32 q with bf16 cache
+    assert _decode(q_dt=0, cache_dt=2) == -2        # fp8 cache needs a bf16 query
+    assert _decode(R=128) == -2 and _decode(P=0) == -2
+    assert _decode(B=-1) == -1 and _decode(H=0) == -1 and _decode(S=0) == -1
+    assert _decode(bs=0) == -1 and _decode(nb=0) == -1 and _decode(maxblk=0) == -1
+    assert _decode(bstride=100) == -1 and _decode(bts=5) == -1
+    assert _decode(qsb=0) == -1 and _decode(qsh=0) == -1
+    assert _decode(sm=float("nan")) == -1 and _decode(sm=float("inf")) == -1
+    assert _decode(cache_dt=2) == -1                # fp8 cache without kv_scale
+    assert _decode(kvs=FAKE) == -1                  # kv_scale with a bf16 cache
+    for k in ["q", "cache", "bt", "seq", "ws", "o", "lse"]:
+        assert _decode(**{k: None}) == -1, k
+    assert _decode(ws=FAKE + 2) == -1               # misaligned workspace
+    assert _decode(wsb=4 * 128 * 4 * 513 * 4 - 4) == -3
+    assert _decode(S=5) == -3                       # workspace sized for 4 splits
+    assert _decode(B=0) == 0                        # empty batch: nothing launched
+
+
+def test_decode_ex_validation():
+    O_ = binding.DecodeOpts
+    assert _decode(O_(3, 0, 0, 0)) == -1
+    assert _decode(O_(0, 3, 0, 0)) == -1
+    assert _decode(O_(0, 0, -1, 0)) == -1
+    assert _decode(O_(0, 2, 0, 0), q_dt=0, cache_dt=0) == -2   # MFMA kernel needs a bf16 query
+    assert _decode(O_(0, 0, 0, 0), B=0) == 0

@@ -1,0 +1,245 @@
+"""GPU edge cases and invariances, each against the oracle (or bit-exact
+against another GPU run where the property is exact):
+
+* every stage-1 kernel configuration (heads per workgroup 16/32/64/128),
+  both partitions, several grids;
+* a late token whose score jumps far above the earlier maximum (the decode
+  must redo the range with a larger softmax reference);
+* block sizes 1, 16, 48, 64 (1 exceeds the staged block-table window);
+* empty and single-token requests, head counts that are not multiples of 16;
+* strided kv_c/k_pe views (the projection-output layout) and an unaligned view;
+* NaN in every unwritten cache slot never reaching o or lse;
+* bit-exact invariance to the physical block permutation (same split count)
+  and batch invariance with num_kv_splits = 1.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mla_paged_decode_concat_amd as M
+from mla_paged_decode_concat_amd import workloads as W
+from oracle import mla_oracle as O
+
+from helpers import compare, oracle_cache, oracle_decode
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+SM = W.SM_SCALE
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def _write(bt):
+    M.cache_write(bt.kv_c, bt.k_pe, bt.cache, bt.slot_mapping, "fp8" if bt.spec.cache_dtype == "fp8" else "auto",
+                  bt.scale)
+    torch.cuda.synchronize()
+
+
+def _decode(bt, S, **kw):
+    o, lse = M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, SM, S, bt.spec.R, kv_scale=bt.scale, **kw)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("hpg", [16, 32, 64, 128])
+@pytest.mark.parametrize("partition", [1, 2])
+def test_mfma_head_groups_v3_shape(hpg, partition):
+    bt = W.make_batch(2, DEV, B=2, seq_lens=[1000, 777])
+    ref_cache = oracle_cache(bt)
+    _write(bt)
+    o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
+    for S in [1, 3, 16]:
+        _print(f"[mfma] hpg={hpg} partition={partition} S={S}")
+        o, lse = _decode(bt, S, kernel=2, heads_per_group=hpg, partition=partition)
+        compare(o, lse, o_ref, lse_ref, "bf16")
+
+
+@pytest.mark.parametrize("grid", [1, 7, 64, 1000])
+def test_balanced_grid_sizes(grid):
+    bt = W.make_batch(1, DEV, B=9, max_len=2500)
+    ref_cache = oracle_cache(bt)
+    _write(bt)
+    o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
+    for S in [2, 5, 8]:
+        _print(f"[grid] G={grid} S={S}")
+        for kernel in [1, 2]:
+            o, lse = _decode(bt, S, kernel=kernel, partition=2, grid=grid)
+            compare(o, lse, o_ref, lse_ref, "bf16")
+
+
+def test_late_dominant_token_forces_redo():
+    """Scores of the last tokens sit far above every earlier score: the
+    decode's softmax reference set on the first tile cannot represent them,
+    so the range is redone; results still match the oracle."""
+    bt = W.make_batch(2, DEV, B=2, seq_lens=[700, 1500])
+    # q and the rows' rope part aligned on a few late tokens: score ~ +200
+    with torch.no_grad():
+        n0 = bt.seq_lens_list[0]
+        rows = bt.last_token_rows  # last token of each request
+        for b in range(2):
+            r = int(rows[b])
+            for back in [0, 5, 33]:          # three late tokens per request
+                bt.k_pe[r - back] = 0
+                bt.k_pe[r - back, :16] = 4.0
+        bt.q[:, :, 512:] = 0
+        bt.q[:, :, 512:528] = 4.0            # 16 * 4 * 4 = 256 raw -> ~18 after sm_scale
+        bt.q[:, :, 512:528] *= 12.0          # -> raw 3072, score ~ 222 (natural units)
+    ref_cache = oracle_cache(bt)
+    _write(bt)
+    o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
+    assert np.all(lse_ref > 150)
+    for hpg in [32, 128]:
+        for S in [1, 4]:
+            _print(f"[redo] hpg={hpg} S={S}")
+            o, lse = _decode(bt, S, kernel=2, heads_per_group=hpg)
+            compare(o, lse, o_ref, lse_ref, "bf16")
+
+
+@pytest.mark.parametrize("bs", [1, 16, 48, 64])
+def test_block_sizes(bs):
+    spec = W.SPECS[1]
+    lens = [1, 31, 33, 1500, 2049]
+    bt = W.make_batch(1, DEV, seq_lens=lens)
+    # rebuild the paging with block size bs over the same token rows
+    nblk = [-(-n // bs) for n in lens]
+    g = torch.Generator().manual_seed(bs)
+    perm = torch.randperm(sum(nblk) + 1, generator=g)
+    table = torch.full((len(lens), max(nblk)), int(perm[-1]), dtype=torch.int32)
+    slots, off = [], 0
+    for b, n in enumerate(lens):
+        ids = perm[off:off + nblk[b]]
+        off += nblk[b]
+        table[b, :nblk[b]] = ids.to(torch.int32)
+        j = torch.arange(n)
+        slots.append(ids[j // bs] * bs + j % bs)
+    bt.block_table = table.to(DEV)
+    bt.slot_mapping = torch.cat(slots).to(DEV)
+    bt.cache = torch.full((sum(nblk) + 1, bs, spec.D), W.NAN_BF16, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    ref_cache = O.cache_write(W.bits(bt.cache), W.bits(bt.kv_c), W.bits(bt.k_pe), bt.slot_mapping.cpu().numpy(),
+                              "bf16", "bf16")
+    _write(bt)
+    assert np.array_equal(bt.cache.cpu().view(torch.int16).numpy().view(np.uint16), ref_cache)
+    o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
+    for S in [1, 4]:
+        for kernel in [1, 2]:
+            for partition in [1, 2]:
+                _print(f"[bs] bs={bs} S={S} kernel={kernel} partition={partition}")
+                o, lse = _decode(bt, S, kernel=kernel, partition=partition)
+                compare(o, lse, o_ref, lse_ref, "bf16")
+
+
+def test_empty_and_single_token_requests():
+    bt = W.make_batch(2, DEV, seq_lens=[0, 1, 0, 65, 1])
+    ref_cache = oracle_cache(bt)
+    _write(bt)
+    o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
+    assert np.isneginf(lse_ref[0]).all() and np.isneginf(lse_ref[2]).all()
+    for S in [1, 2, 7]:
+        for kernel in [1, 2]:
+            for partition in [1, 2]:
+                o, lse = _decode(bt, S, kernel=kernel, partition=partition)
+                compare(o, lse, o_ref, lse_ref, "bf16")
+                assert torch.all(o[0] == 0) and torch.all(o[2] == 0)
+
+
+@pytest.mark.parametrize("H", [1, 5, 24, 40, 48])
+def test_head_counts_not_multiple_of_16(H):
+    bt = W.make_batch(1, DEV, B=3, max_len=300, H=H)
+    ref_cache = oracle_cache(bt)
+    _write(bt)
+    o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
+    for S in [1, 3]:
+        o, lse = _decode(bt, S)            # auto picks a kernel that supports H
+        compare(o, lse, o_ref, lse_ref, "bf16")
+
+
+def test_strided_inputs_and_unaligned_view():
+    """kv_c and k_pe as column slices of one [T, 576] projection output, and
+    a view whose rows are not 16-byte aligned (element-wise write path)."""
+    bt = W.make_batch(1, DEV, B=4, max_len=200)
+    T = bt.kv_c.shape[0]
+    big = torch.cat([bt.kv_c, bt.k_pe], dim=1).contiguous()
+    ref_cache = oracle_cache(bt)
+    M.cache_write(big[:, :512], big[:, 512:], bt.cache, bt.slot_mapping, "auto")
+    torch.cuda.synchronize()
+    assert np.array_equal(bt.cache.cpu().view(torch.int16).numpy().view(np.uint16), ref_cache)
+    odd = torch.zeros((T, 577 + 3), dtype=torch.bfloat16, device=DEV)
+    odd[:, 1:513] = bt.kv_c
+    odd[:, 513:577] = bt.k_pe
+    bt.cache.view(torch.int16).fill_(W.NAN_BF16)
+    M.cache_write(odd[:, 1:513], odd[:, 513:577], bt.cache, bt.slot_mapping, "auto")
+    torch.cuda.synchronize()
+    assert np.array_equal(bt.cache.cpu().view(torch.int16).numpy().view(np.uint16), ref_cache)
+
+
+def test_nan_poison_never_leaks():
+    """Unwritten slots (tails of last pages, the spare block used as table
+    padding) hold NaN; outputs stay finite and match the oracle."""
+    bt = W.make_batch(3, DEV, B=12, max_len=700)      # block 16, ragged tails, 10% pad rows
+    ref_cache = oracle_cache(bt)
+    _write(bt)
+    c = bt.cache.float()
+    assert torch.isnan(c).any()                       # poison is present
+    o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
+    for S in [1, 5]:
+        o, lse = _decode(bt, S)
+        assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+        compare(o, lse, o_ref, lse_ref, "bf16")
+
+
+def test_block_permutation_invariance_bit_exact():
+    """The same logical sequences under two different physical block
+    assignments decode to identical bits (same num_kv_splits)."""
+    a = W.make_batch(2, DEV, B=3, seq_lens=[800, 1500, 64], seed=5)
+    b = W.make_batch(2, DEV, B=3, seq_lens=[800, 1500, 64], seed=5)
+    # re-assign b's physical blocks with another permutation
+    g = torch.Generator().manual_seed(99)
+    perm = torch.randperm(b.num_blocks, generator=g).to(DEV)
+    old_table = b.block_table.long()
+    b.block_table = perm[old_table].to(torch.int32)
+    bsz = b.spec.block_size
+    b.slot_mapping = perm[b.slot_mapping // bsz] * bsz + b.slot_mapping % bsz
+    _write(a)
+    _write(b)
+    for S in [1, 4, 16]:
+        for kernel in [1, 2]:
+            oa, la = _decode(a, S, kernel=kernel)
+            ob, lb = _decode(b, S, kernel=kernel)
+            assert torch.equal(oa, ob) and torch.equal(la, lb)
+
+
+def test_batch_invariance_single_split():
+    """num_kv_splits = 1: a request decodes to the same bits alone and inside
+    a batch."""
+    full = W.make_batch(1, DEV, B=6, max_len=3000)
+    _write(full)
+    o, lse = _decode(full, 1)
+    for b in [0, 3, 5]:
+        o1, l1 = M.decode(full.q[b:b + 1].contiguous(), full.cache, full.block_table[b:b + 1].contiguous(),
+                          full.seq_lens[b:b + 1].contiguous(), SM, 1, 512)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0], o[b]) and torch.equal(l1[0], lse[b])
+
+
+def test_fp8_write_every_bf16_pattern():
+    """All 65536 bf16 bit patterns through the fp8 write, compared with the
+    oracle's encoder (covers subnormals, ties, saturation and NaN)."""
+    pats = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    T = 65536 // 512
+    kv_c = pats.reshape(T, 512).to(DEV)
+    k_pe = pats[:T * 64].reshape(T, 64).to(DEV)
+    cache = torch.full((T, 1, 576), 0x7F, dtype=torch.uint8, device=DEV)
+    slots = torch.arange(T, dtype=torch.int64, device=DEV)
+    for sc in [1.0, 9.5 / 448.0, 0.0213, 3.7, 1e-30]:
+        scale = torch.tensor([sc], dtype=torch.float32, device=DEV)
+        M.cache_write(kv_c, k_pe, cache, slots, "fp8", scale)
+        torch.cuda.synchronize()
+        ref = O.cache_write(np.full((T, 1, 576), 0x7F, np.uint8), W.bits(kv_c), W.bits(k_pe), slots.cpu().numpy(),
+                            "bf16", "fp8", float(np.float32(sc)))
+        assert np.array_equal(cache.cpu().numpy(), ref), sc
