@@ -12,10 +12,10 @@
 //    KV tile is read from HBM once and shared by every head (the Triton
 //    prior art re-reads it per 16-head group).
 //  * Tiles stream HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging),
-//    STAGES tiles in flight.  Inside a tile, 16 tokens x 64 bytes form one
-//    1 KB block written by one load instruction; the slot swizzle
-//    16*q + (t ^ (12*(q & 1))) keeps both LDS read patterns below free of
-//    bank conflicts.
+//    STAGES tiles in flight.  Inside a tile, 8 tokens x 128 bytes (full
+//    cache lines) form one 1 KB block written by one load instruction; the
+//    slot swizzle 8*t + (c ^ (2*(t >> 1) + (tq & 1))) keeps both LDS read
+//    patterns below free of bank conflicts.
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: A = K rows from LDS
 //    (ds_read_b128), B = Q^T kept in registers for the whole range.
 //  * O^T = V^T P^T: A = V^T via ds_read_b64_tr_b16 (4 tokens x 1 column per
@@ -105,22 +105,34 @@ struct Stage1 {
     wait_vmcnt<0>();
   }
 
+  // Tile layout in LDS: block (cq8, tq) = chunks 8*cq8 .. +7 (16 bytes each)
+  // of tokens 8*tq .. +7, at byte (4*cq8 + tq) * 1024; inside it token t8,
+  // chunk c8 sits in 16-byte slot 8*t8 + (c8 ^ swz(t8, tq)).  One load
+  // instruction fills one block: lane i takes token i / 8 and the chunk whose
+  // slot is i, so each group of 8 lanes reads one full 128-byte line.
+  static __device__ __forceinline__ int swz(int t8, int tq) { return 2 * (t8 >> 1) + (tq & 1); }
+
   static __device__ __forceinline__ void issue_tile(const DecodeParams& p, int tile_start, int se, int pg0,
-                                                    char* buf, const int* s_table, int tt_dma, int wave, int g) {
+                                                    char* buf, const int* s_table, int wave, int lane) {
     const char* cache = reinterpret_cast<const char*>(p.cache);
-    const char* rows[2];
+    const int t8 = lane >> 3, x = lane & 7;
+    // token quarters this wave loads: wave, wave + NW, ... (mod 4)
+    constexpr int NQ = NW >= 4 ? 1 : 4 / NW;
+    const char* rows[NQ];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      int tok = tile_start + 16 * tb + tt_dma;
+    for (int j = 0; j < NQ; ++j) {
+      const int tq = (wave + NW * j) & 3;
+      int tok = tile_start + 8 * tq + t8;
       tok = tok < se ? tok : se - 1;              // past the range: re-read a valid row (masked later)
       const int pg = tok / p.block_size;
       const long long page = s_table[pg - pg0];
-      rows[tb] = cache + (page * p.block_stride + (long long)(tok - pg * p.block_size) * G::D) * 2;
+      rows[j] = cache + (page * p.block_stride + (long long)(tok - pg * p.block_size) * G::D) * 2;
     }
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      const int kb = wave + NW * i;
-      const char* src = rows[kb & 1] + (4 * (kb >> 1) + g) * 16;
+      const int kb = wave + NW * i;                 // block: cq8 = kb / 4, tq = kb % 4
+      const int tq = kb & 3, cq8 = kb >> 2;
+      const char* src = rows[i % NQ] + (8 * cq8 + (x ^ swz(t8, tq))) * 16;
       dma16(src, lds_addr(buf) + kb * 1024);
     }
   }
@@ -155,21 +167,25 @@ struct Stage1 {
     const float c2 = p.sm_scale * kLog2e;
 
     // lane-constant LDS offsets
-    // K rows (A operand of QK): token r16 of a 16-token block, chunk 4ks + g
-    const uint32_t k_off = (uint32_t)((16 * g + (r16 ^ (12 * (g & 1)))) * 16);
-    // V^T (A operand of PV) via transpose reads: this lane addresses token
-    // 4g + (r16 >> 2), bytes [8 * (r16 & 3), +8) of a 16-column block
-    uint32_t v_off[2];
+    // K rows (A operand of QK): token m = r16 of a 16-token block, chunk 4ks + g;
+    // k_off[ks & 1] is the lane part, the block part is compile-time
+    uint32_t k_off[2];
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
-      const int s = r16 & 3;
-      const int q = 2 * par + (s >> 1);
-      const int tt = 4 * g + (r16 >> 2);
-      v_off[par] = (uint32_t)((16 * q + (tt ^ (12 * (q & 1)))) * 16 + (s & 1) * 8);
+      const int t8 = r16 & 7, tqo = r16 >> 3, c8 = 4 * par + g;
+      k_off[par] = (uint32_t)(tqo * 1024 + (8 * t8 + (c8 ^ swz(t8, tqo))) * 16);
     }
-    // DMA role: slot `lane` of a block holds token tt_dma of its 16, chunk 4cq + g
-    const int tt_dma = r16 ^ (12 * (g & 1));
-
+    // V^T (A operand of PV) via transpose reads: this lane addresses token
+    // 16tb + 4g + (r16 >> 2), bytes [8 * (r16 & 3), +8) of a 16-column block;
+    // v_off[cb & 3] is the lane part
+    uint32_t v_off[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int sg = r16 & 3;
+      const int t8 = 4 * (g & 1) + (r16 >> 2), tqo = g >> 1;
+      const int c8 = 2 * k + (sg >> 1);
+      v_off[k] = (uint32_t)(tqo * 1024 + (8 * t8 + (c8 ^ swz(t8, tqo))) * 16 + (sg & 1) * 8);
+    }
     const int bs = p.block_size;
     const int32_t* btab = p.block_table + (long long)b * p.bt_stride;
 
@@ -212,7 +228,7 @@ struct Stage1 {
         const int ntiles = (se - sa + kTile - 1) / kTile;
 #pragma unroll
         for (int t = 0; t < STAGES - 1; ++t)
-          if (t < ntiles) issue_tile(p, sa + kTile * t, se, pg0, smem + t * G::TILE_BYTES, s_table, tt_dma, wave, g);
+          if (t < ntiles) issue_tile(p, sa + kTile * t, se, pg0, smem + t * G::TILE_BYTES, s_table, wave, lane);
 
 #pragma unroll 1
         for (int t = 0; t < ntiles; ++t) {
@@ -226,7 +242,7 @@ struct Stage1 {
           }
           if (t + STAGES - 1 < ntiles)
             issue_tile(p, sa + kTile * (t + STAGES - 1), se, pg0,
-                       smem + ((t + STAGES - 1) % STAGES) * G::TILE_BYTES, s_table, tt_dma, wave, g);
+                       smem + ((t + STAGES - 1) % STAGES) * G::TILE_BYTES, s_table, wave, lane);
           const char* tile = smem + (t % STAGES) * G::TILE_BYTES;
           const int tile_start = sa + kTile * t;
 
@@ -241,14 +257,16 @@ struct Stage1 {
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) kr[ks][mb] = *MLA_LDS(const bf16x8_t, tile + (2 * ks + mb) * 1024 + k_off);
+            for (int mb = 0; mb < 2; ++mb)
+              kr[ks][mb] = *MLA_LDS(const bf16x8_t, tile + ((ks >> 1) * 4 + 2 * mb) * 1024 + k_off[ks & 1]);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int ks = 0; ks < G::KS; ++ks) {
             if (ks + 2 < G::KS) {
 #pragma unroll
               for (int mb = 0; mb < 2; ++mb)
-                kr[(ks + 2) % 3][mb] = *MLA_LDS(const bf16x8_t, tile + (2 * (ks + 2) + mb) * 1024 + k_off);
+                kr[(ks + 2) % 3][mb] =
+                    *MLA_LDS(const bf16x8_t, tile + (((ks + 2) >> 1) * 4 + 2 * mb) * 1024 + k_off[ks & 1]);
             }
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
@@ -307,9 +325,9 @@ struct Stage1 {
           // ---- O^T += V^T P^T  (CB column blocks x NB head blocks); V^T read
           // two column blocks ahead through a 3-slot ring
           auto vread = [&](int cb) -> bf16x8_t {
-            const char* vb = tile + (cb >> 1) * 2048 + v_off[cb & 1];
+            const char* vb = tile + (cb >> 2) * 4096 + v_off[cb & 3];
             const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(MLA_LDS(bf16x4_t, vb));
-            const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(MLA_LDS(bf16x4_t, vb + 1024));
+            const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(MLA_LDS(bf16x4_t, vb + 2048));
             return bf16x8_t{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
           };
           __builtin_amdgcn_sched_barrier(0);
@@ -452,12 +470,11 @@ bool mfma_supported(int H, int R, int cache_dtype) {
 
 bool mfma_group_ok(int hpg) { return hpg == 16 || hpg == 32 || hpg == 64 || hpg == 128; }
 
-// Heads per workgroup.  With one partial per request (num_kv_splits == 1)
-// there are only B token ranges, so the heads are spread over more
-// workgroups (their shared tiles meet in L2); otherwise one workgroup takes
-// up to 128 heads and reads each tile once.
+// Heads per workgroup: one workgroup takes up to 128 heads (4 waves of 32)
+// and reads each tile once; the smaller groups exist for head counts that
+// 128 does not divide.
 int mfma_heads_per_group(int H, int S) {
-  if (S == 1 && H % 32 == 0) return 32;
+  (void)S;
   if (H % 128 == 0) return 128;
   if (H % 64 == 0) return 64;
   if (H % 32 == 0) return 32;
