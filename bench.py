@@ -62,6 +62,37 @@ class HipEvent:
             HipEvent._hip.hipEventDestroy(self.handle)
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_v3_b64_h128_n8192_hbm_traffic.txt")
+
+
+def kernel_sources_sha256() -> str:
+    """sha256 over the HIP sources of the library (file names and bytes)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "mla_paged_decode_concat_amd", "csrc", "*"))):
+        if p.endswith((".hip", ".h")):
+            h.update(os.path.basename(p).encode())
+            with open(p, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """Stage-1 HBM bytes per launch (read + write) from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary, calibrated against a plain
+    device copy; None when the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            line = [l for l in f if l.startswith("machine:")][-1]
+    except (OSError, IndexError):
+        return None
+    kv = dict(t.split("=", 1) for t in line.split()[1:] if "=" in t)
+    if kv.get("source_sha256") != kernel_sources_sha256():
+        return None
+    return int(kv["stage1_read_bytes"]) + int(kv["stage1_write_bytes"])
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,7 +240,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
         },
         "kv_read_gbps": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "stage1_us": round(st1_ms * 1e3, 2),
