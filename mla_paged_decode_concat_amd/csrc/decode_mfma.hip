@@ -24,10 +24,16 @@
 //    B-operand layout once the 8 k-slots of a lane are bound to tokens
 //    {4g..4g+3, 16+4g..16+4g+3}.  Every per-head quantity therefore lives in
 //    the lane that owns the head; nothing moves across lanes per tile.
-//  * Lazy rescaling: a head's running max only moves when the tile max
-//    exceeds it by more than 8 (log2 units), so exp2(s - m) <= 256 and the
-//    O rescale is rare.  acc and l always share the same reference max, so
-//    the result is the exact softmax.
+//  * Fixed softmax reference: each head's reference is set on the first tile
+//    of a pass and p = 2^(s - ref) is accumulated unscaled; a tile more than
+//    32 (log2 units) above the reference makes the workgroup redo its range
+//    with the larger reference.  acc and l always share the reference, so the
+//    result is the exact softmax, and acc is never multiplied (which keeps it
+//    in the accumulation registers).
+//  * Each CU keeps only about 36-40 KB of loads in flight before a further
+//    load issue stalls the issuing wave, so a workgroup gets about one tile
+//    per HBM round trip; the loads of a tile are issued in one burst after
+//    the tile barrier, three tiles ahead.
 //  * The request's block-table slice is staged in LDS, so page lookups are
 //    LDS reads and never wait behind the tile loads on the vmcnt counter.
 //  * Workgroups that share a token range (different head groups) get ids
@@ -35,6 +41,8 @@
 //    meet in that XCD's L2.
 #include "mla_device.h"
 #include "mla_launch.h"
+
+#include <utility>
 
 namespace mla {
 
@@ -70,20 +78,104 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// 16 bytes per lane HBM -> LDS (global_load_lds_dwordx4): lane i's bytes land
-// at LDS address lds_base + 16 * i.  Issued through inline asm so the compiler
-// does not add a full vmcnt drain before every later LDS read (it cannot
-// prove the in-flight tile and the tile being read are disjoint); the kernel
-// orders them itself with wait_vmcnt + a workgroup barrier.
+// 16 bytes per lane HBM -> LDS (global_load_lds_dwordx4): lane i reads
+// gptr + OFF and its bytes land at LDS address lds_base + 16 * i.  The
+// instruction's immediate offset is added to the LDS address too (M0 + OFF +
+// 16 i), so M0 is set to lds_base - OFF; callers keep lds_base >= OFF.  The
+// ISA asks for one wait state between writing M0 and the load.  Issued
+// through inline asm so the compiler does not add a full vmcnt drain before
+// every later LDS read (it cannot prove the in-flight tile and the tile being
+// read are disjoint); the kernel orders them itself with wait_vmcnt + a
+// workgroup barrier.
+template <int OFF>
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
-               "s"(__builtin_amdgcn_readfirstlane(lds_base))
+  static_assert(OFF >= 0 && OFF < 4096, "immediate offset");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2" ::"v"(gptr),
+               "s"(__builtin_amdgcn_readfirstlane(lds_base - OFF)), "i"(OFF)
                : "memory");
+}
+
+// This lane's index, read so that the compiler cannot hoist what is derived
+// from it out of a loop: per-lane address terms are then recomputed (a few
+// instructions) instead of being kept live across the tile loop, where they
+// would push the register budget over and get spilled (a scratch reload
+// waits on the same counter as the tile loads in flight).
+__device__ __forceinline__ int lane_now() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(size_t)MLA_LDS(const char, p);
 }
+
+// compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1
+template <class F, int... I>
+__device__ __forceinline__ void static_for_(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_(f, std::make_integer_sequence<int, N>{});
+}
+
+// Tile loads.  Tile layout in LDS: block (cq8, tq) = chunks 8*cq8 .. +7 (16
+// bytes each) of tokens 8*tq .. +7, at byte (4*cq8 + tq) * 1024; inside it
+// token t8, chunk c8 sits in 16-byte slot 8*t8 + (c8 ^ swz(t8, tq)).  One
+// load instruction fills one block: lane i takes token i / 8 and the chunk
+// whose slot is i, so each group of 8 lanes reads one full 128-byte line.
+// With NW waves sharing a tile, wave w loads token quarters w, w + NW, ...;
+// its load i fills block (cq8 = i / NQ, tq = w + NW * (i % NQ)), from one
+// per-quarter lane address plus the immediate offset 128 * cq8 (the block
+// sits at 1024 * (4 cq8 + tq) >= 128 cq8 bytes, as dma16 requires).
+template <int R, int NW>
+struct TileLoad {
+  using G = Geo<R>;
+  static_assert(NW == 1 || NW == 2 || NW == 4, "waves per tile");
+  static constexpr int NQ = 4 / NW;                // token quarters per wave
+  static constexpr int LPW = G::NBLK / NW;         // load instructions per wave per tile
+  static_assert(G::NBLK % NW == 0, "tile blocks must split evenly over the waves");
+  static __device__ __forceinline__ int swz(int t8, int tq) { return 2 * (t8 >> 1) + (tq & 1); }
+
+  struct Rows {
+    const char* r[NQ];
+  };
+  static __device__ __forceinline__ Rows rows(const DecodeParams& p, int tile_start, int se, int pg0,
+                                              const int* s_table, int wave) {
+    const char* cache = reinterpret_cast<const char*>(p.cache);
+    const int lane = lane_now();
+    const int t8 = lane >> 3, x = lane & 7;
+    Rows rw;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int tq = wave + NW * j;
+      int tok = tile_start + 8 * tq + t8;
+      tok = tok < se ? tok : se - 1;              // past the range: re-read a valid row (masked later)
+      const int pg = tok / p.block_size;
+      const long long page = s_table[pg - pg0];
+      rw.r[j] = cache + (page * p.block_stride + (long long)(tok - pg * p.block_size) * G::D) * 2 +
+                (x ^ swz(t8, tq)) * 16;
+    }
+    return rw;
+  }
+  // a tile's column groups cq8 < CQ-1 (values) go to vbuf, the last (rope) to rbuf
+  static constexpr int CQ = G::CHUNKS / 8;
+  template <int I>
+  static __device__ __forceinline__ void issue(const Rows& rw, const char* vbuf, const char* rbuf, int wave) {
+    constexpr int j = I % NQ, cq8 = I / NQ;
+    if constexpr (cq8 < CQ - 1)
+      dma16<128 * cq8>(rw.r[j], lds_addr(vbuf) + (wave + NW * j + 4 * cq8) * 1024);
+    else
+      dma16<128 * cq8>(rw.r[j], lds_addr(rbuf) + (wave + NW * j) * 1024);
+  }
+  static __device__ __forceinline__ void tile(const DecodeParams& p, int tile_start, int se, int pg0,
+                                              const char* vbuf, const char* rbuf, const int* s_table, int wave,
+                                              int lane) {
+    const Rows rw = rows(p, tile_start, se, pg0, s_table, wave);
+    static_for<LPW>([&](auto i) { issue<decltype(i)::value>(rw, vbuf, rbuf, wave); });
+  }
+};
 
 template <int R, int NB, int NW, int STAGES>
 struct Stage1 {
@@ -92,7 +184,9 @@ struct Stage1 {
   static_assert(G::NBLK % NW == 0, "tile blocks must split evenly over the waves");
   static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
   static constexpr int HPG = 16 * NB * NW;         // heads per workgroup
+  static constexpr int NW_ = NW;
   static constexpr int SMEM = STAGES * G::TILE_BYTES;
+  static constexpr int TABLE = kTableWindow;       // block-table window staged in LDS
 
   // wait until the loads of the tile that has `after` newer tiles in flight landed
   static __device__ __forceinline__ void wait_tile(int after) {
@@ -105,36 +199,10 @@ struct Stage1 {
     wait_vmcnt<0>();
   }
 
-  // Tile layout in LDS: block (cq8, tq) = chunks 8*cq8 .. +7 (16 bytes each)
-  // of tokens 8*tq .. +7, at byte (4*cq8 + tq) * 1024; inside it token t8,
-  // chunk c8 sits in 16-byte slot 8*t8 + (c8 ^ swz(t8, tq)).  One load
-  // instruction fills one block: lane i takes token i / 8 and the chunk whose
-  // slot is i, so each group of 8 lanes reads one full 128-byte line.
-  static __device__ __forceinline__ int swz(int t8, int tq) { return 2 * (t8 >> 1) + (tq & 1); }
-
+  static __device__ __forceinline__ int swz(int t8, int tq) { return TileLoad<R, NW>::swz(t8, tq); }
   static __device__ __forceinline__ void issue_tile(const DecodeParams& p, int tile_start, int se, int pg0,
                                                     char* buf, const int* s_table, int wave, int lane) {
-    const char* cache = reinterpret_cast<const char*>(p.cache);
-    const int t8 = lane >> 3, x = lane & 7;
-    // token quarters this wave loads: wave, wave + NW, ... (mod 4)
-    constexpr int NQ = NW >= 4 ? 1 : 4 / NW;
-    const char* rows[NQ];
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      const int tq = (wave + NW * j) & 3;
-      int tok = tile_start + 8 * tq + t8;
-      tok = tok < se ? tok : se - 1;              // past the range: re-read a valid row (masked later)
-      const int pg = tok / p.block_size;
-      const long long page = s_table[pg - pg0];
-      rows[j] = cache + (page * p.block_stride + (long long)(tok - pg * p.block_size) * G::D) * 2;
-    }
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int kb = wave + NW * i;                 // block: cq8 = kb / 4, tq = kb % 4
-      const int tq = kb & 3, cq8 = kb >> 2;
-      const char* src = rows[i % NQ] + (8 * cq8 + (x ^ swz(t8, tq))) * 16;
-      dma16(src, lds_addr(buf) + kb * 1024);
-    }
+    TileLoad<R, NW>::tile(p, tile_start, se, pg0, buf, buf + (G::CHUNKS / 8 - 1) * 4096, s_table, wave, lane);
   }
 
   // Token range [a, e) of request b for this wave's heads; writes partial `part`.
@@ -144,6 +212,7 @@ struct Stage1 {
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 4;
     const int r16 = lane & 15;
+    head0 += wave * 16 * NB;                   // this wave's heads
 
     // ---- Q^T operand in registers: lane = head r16 of block nb, dims 32ks + 8g .. +8
     bf16x8_t qf[NB][G::KS];
@@ -373,13 +442,17 @@ struct Stage1 {
   }
 };
 
-// Workgroup id -> (work item, head group): the head groups of one item get
-// ids id, id+8, id+16, ... (same XCD, dispatched together).
+// Workgroup id -> (work item, head group).  The dispatcher sends id i to XCD
+// i % 8; consecutive items (neighbouring token ranges, which share requests,
+// their queries and block-table rows) are kept on one XCD, and the head
+// groups of one item (which share every KV tile) are dispatched together on
+// that XCD, so the shared data meets in its L2.
 __device__ __forceinline__ bool map_block(int id, int items, int groups, int& item, int& hg) {
+  const int per_xcd = (items + kXcds - 1) / kXcds;
   const int x = id % kXcds;
   const int j = id / kXcds;
   hg = j % groups;
-  item = x + kXcds * (j / groups);
+  item = x * per_xcd + j / groups;
   return item < items;
 }
 
@@ -387,14 +460,12 @@ __host__ __device__ inline int mapped_grid(int items, int groups) {
   return ((items + kXcds - 1) / kXcds) * kXcds * groups;
 }
 
-template <int R, int NB, int NW, int STAGES>
-__global__ __launch_bounds__(NW * 64) void stage1_mfma_kernel(DecodeParams p) {
-  using K = Stage1<R, NB, NW, STAGES>;
+template <class K>
+__global__ __launch_bounds__(K::NW_ * 64) void stage1_mfma_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[K::SMEM];
-  __shared__ int s_table[kTableWindow];
+  __shared__ int s_table[K::TABLE];
   __shared__ int s_flags[2];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int groups = p.H / K::HPG;
 
   // Enumerate this workgroup's pieces (request, token range, partial index)
@@ -402,7 +473,7 @@ __global__ __launch_bounds__(NW * 64) void stage1_mfma_kernel(DecodeParams p) {
   const bool literal = p.partition == PART_LITERAL;
   int item, hg;
   if (!map_block(blockIdx.x, literal ? p.B * p.S : p.G, groups, item, hg)) return;
-  const int head0 = hg * K::HPG + wave * 16 * NB;
+  const int head0 = hg * K::HPG;
   long long Q = 0, lo = 0, hi = 0, carry = 0;
   int base = 0;
   unsigned long long mask = 0;
@@ -487,24 +558,22 @@ constexpr int stages_for() {
   return (2 * (Geo<R>::NBLK / NW) < 64) ? 4 : 3;
 }
 
-template <int R, int NB, int NW>
-static hipError_t launch_cfg(const DecodeParams& p, hipStream_t stream) {
-  constexpr int STAGES = stages_for<R, NW>();
-  using K = Stage1<R, NB, NW, STAGES>;
+template <class K>
+static hipError_t launch_k(const DecodeParams& p, hipStream_t stream) {
   const int groups = (p.H + K::HPG - 1) / K::HPG;
   const int items = p.partition == PART_LITERAL ? p.B * p.S : p.G;
-  dim3 grid((unsigned)mapped_grid(items, groups)), block(NW * 64);
-  hipLaunchKernelGGL((stage1_mfma_kernel<R, NB, NW, STAGES>), grid, block, 0, stream, p);
+  dim3 grid((unsigned)mapped_grid(items, groups)), block(K::NW_ * 64);
+  hipLaunchKernelGGL((stage1_mfma_kernel<K>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
 template <int R>
 static hipError_t launch_r(const DecodeParams& p, hipStream_t stream) {
   switch (p.heads_per_group) {
-    case 128: return launch_cfg<R, 2, 4>(p, stream);
-    case 64: return launch_cfg<R, 2, 2>(p, stream);
-    case 32: return launch_cfg<R, 2, 1>(p, stream);
-    case 16: return launch_cfg<R, 1, 1>(p, stream);
+    case 128: return launch_k<Stage1<R, 2, 4, stages_for<R, 4>()>>(p, stream);
+    case 64: return launch_k<Stage1<R, 2, 2, stages_for<R, 2>()>>(p, stream);
+    case 32: return launch_k<Stage1<R, 2, 1, stages_for<R, 1>()>>(p, stream);
+    case 16: return launch_k<Stage1<R, 1, 1, stages_for<R, 1>()>>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
