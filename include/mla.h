@@ -65,9 +65,13 @@ const char* mla_status_string(int status);
 int mla_num_kv_splits(int64_t max_seq_len, int num_cus, int batch_invariant);
 
 /*
- * Bytes of the fp32 split workspace [B, H, num_kv_splits, kv_lora_rank + 1]:
- * per (request, head, split) the normalised partial output followed by its
- * natural-log LSE.  [ESSAY: Data flow (attn_logits shape, the "+1" LSE slot);
+ * Bytes of the fp32 split workspace: B * H * num_kv_splits * (kv_lora_rank + 1)
+ * values, the size of the pages' [B, H, num_kv_splits, kv_lora_rank + 1]
+ * workspace, holding per (request, head, split) the normalised partial output
+ * and its natural-log LSE.  This library stores the partial outputs as rows
+ * [B, H, num_kv_splits, kv_lora_rank] followed by the LSEs
+ * [B, H, num_kv_splits], so that every row starts on a cache line.
+ * [ESSAY: Data flow (attn_logits shape, the "+1" LSE slot);
  * API: _reserve_attn_logits_workspace sizes it once at the worst case]
  * Host-only.  Returns 0 if any argument is < 1.
  */
@@ -129,8 +133,9 @@ int mla_cache_write(const void* kv_c, int64_t kv_c_row_stride,
  * n == 0 gives o = 0 and lse = -inf.
  *
  * Two stages run on `stream`: stage 1 writes per-split normalised partial
- * outputs and LSEs into `workspace` ([B, H, num_kv_splits, R + 1] fp32);
- * stage 2 merges each request's partials by their LSEs.
+ * outputs and LSEs into `workspace` (fp32; layout at
+ * mla_decode_workspace_bytes); stage 2 merges each request's partials by
+ * their LSEs.
  * num_kv_splits bounds the number of partials per request and sets the
  * workspace shape.  With num_kv_splits == 1 every request is one partial,
  * reduced in a fixed order independent of the rest of the batch (batch-
@@ -151,8 +156,8 @@ int mla_cache_write(const void* kv_c, int64_t kv_c_row_stride,
  *   kv_scale                  : device fp32 scalar, required iff fp8 cache
  *                               (one scale for the whole row: k_scale == v_scale)
  *   workspace                 : >= mla_decode_workspace_bytes(B, H, num_kv_splits, R)
- *                               bytes, 4-byte aligned; contents on entry are ignored
- *   o                         : [B, H, R] contiguous, dtype q_dtype
+ *                               bytes, 16-byte aligned; contents on entry are ignored
+ *   o                         : [B, H, R] contiguous, dtype q_dtype, 16-byte aligned
  *   lse                       : [B, H] contiguous fp32
  * Preconditions (device data): 0 <= seq_lens[b] <= max_blocks_per_seq *
  * block_size; the first ceil(seq_lens[b] / block_size) table entries of each

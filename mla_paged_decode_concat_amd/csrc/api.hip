@@ -92,6 +92,7 @@ int mla_cache_write(const void* kv_c, int64_t kv_c_row_stride,
   p.R = kv_lora_rank;
   p.P = rope_dim;
   p.scale = scale;
+  p.tokens_per_wave = write_tokens_per_wave(num_tokens);
 
   const int ib = elem_bytes(in_dtype), cb = elem_bytes(cache_dtype);
   const int out_vec = 16 / ib * cb;   // bytes written per 16-byte input vector
@@ -137,7 +138,7 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
   if ((cache_dtype == MLA_FP8_E4M3) != (kv_scale != nullptr)) return MLA_ERR_ARG;
   if (B == 0) return MLA_OK;
   if (!q || !cache || !block_table || !seq_lens || !workspace || !o || !lse) return MLA_ERR_ARG;
-  if (reinterpret_cast<uintptr_t>(workspace) % 4 != 0) return MLA_ERR_ARG;
+  if (!aligned16(workspace) || !aligned16(o)) return MLA_ERR_ARG;
   if (workspace_bytes < mla_decode_workspace_bytes(B, H, num_kv_splits, kv_lora_rank)) return MLA_ERR_WORKSPACE;
 
   // stage-1 kernel: MFMA for bf16 queries when the geometry allows it

@@ -432,12 +432,11 @@ struct Stage1 {
       const float inv = 1.0f / l;
       const float lse = (m_ref[nb] + __builtin_amdgcn_logf(l)) * kLn2;
       const int h = head0 + 16 * nb + r16;
-      float* dst = p.ws + (((long long)b * p.H + h) * p.S + part) * (R + 1);
+      float* dst = ws_row(p, b, h, part, R);
 #pragma unroll
       for (int cb = 0; cb < G::CB; ++cb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[16 * cb + 4 * g + i] = acc[cb][nb][i] * inv;
-      if (g == 0) dst[R] = lse;
+        *reinterpret_cast<f32x4_t*>(dst + 16 * cb + 4 * g) = acc[cb][nb] * inv;
+      if (g == 0) *ws_lse(p, b, h, part, R) = lse;
     }
   }
 };

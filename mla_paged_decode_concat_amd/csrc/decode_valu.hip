@@ -115,9 +115,8 @@ __device__ void valu_piece(const DecodeParams& p, int b, int h0, int a, int e, i
       o += sm_acc[w][hh][d] * c;
     }
     if (h < p.H) {
-      float* dst = p.ws + (((long long)b * p.H + h) * S + part) * (R + 1);
-      dst[d] = o / L * kvs;
-      if (d == 0) dst[R] = M + logf(L);
+      ws_row(p, b, h, part, R)[d] = o / L * kvs;
+      if (d == 0) *ws_lse(p, b, h, part, R) = M + logf(L);
     }
   }
   __syncthreads();   // LDS is reused by the next piece
@@ -202,7 +201,9 @@ constexpr int kMergeWaves = 4;
 
 template <int QT, int R>
 __global__ __launch_bounds__(kWave * kMergeWaves) void stage2_merge_kernel(DecodeParams p) {
-  constexpr int RJ = R / kWave;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  constexpr int V4 = R / (4 * kWave);   // 16-byte vectors per lane per partial row
+  constexpr int KC = 8;                 // partial rows whose loads are in flight together
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int hblocks = (p.H + kMergeWaves - 1) / kMergeWaves;
@@ -214,38 +215,64 @@ __global__ __launch_bounds__(kWave * kMergeWaves) void stage2_merge_kernel(Decod
   if (p.partition == PART_LITERAL) {
     k = literal_num_partials(n, p.S);
   } else {
-    const BatchTotals t = batch_totals(p.seq_lens, p.B, lane);
-    const long long Q = balanced_chunk(t, p.G, p.S);
-    k = balanced_num_partials(balanced_start(p.seq_lens, b, lane), n, Q);
+    long long start;
+    const BatchTotals t = batch_totals_and_start(p.seq_lens, p.B, b, lane, start);
+    k = balanced_num_partials(start, n, balanced_chunk(t, p.G, p.S));
   }
-  const long long bh = (long long)b * p.H + h;
-  const float* src = p.ws + bh * p.S * (R + 1);
-  float acc[RJ];
+  k = __builtin_amdgcn_readfirstlane(k);
+  const f32x4* rows = reinterpret_cast<const f32x4*>(ws_row(p, b, h, 0, R));   // partial s at rows + s R / 4
+  const float* lses = ws_lse(p, b, h, 0, R);
+  f32x4 acc[V4];
 #pragma unroll
-  for (int j = 0; j < RJ; ++j) acc[j] = 0.0f;
+  for (int q = 0; q < V4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
   float M = -INFINITY, L = 0.0f;
   if (k > 0) {
-    for (int s = lane; s < k; s += kWave) M = fmaxf(M, src[(long long)s * (R + 1) + R]);
+    f32x4 v[KC][V4];
+    auto load_rows = [&](int s0) {
+#pragma unroll
+      for (int j = 0; j < KC; ++j)
+        if (s0 + j < k)
+#pragma unroll
+          for (int q = 0; q < V4; ++q) v[j][q] = rows[(long long)(s0 + j) * (R / 4) + lane + kWave * q];
+    };
+    load_rows(0);   // in flight while the LSEs are reduced
+    for (int s = lane; s < k; s += kWave) M = fmaxf(M, lses[s]);
     M = wave_max(M);
     float Ls = 0.0f;
-    for (int s = lane; s < k; s += kWave) Ls += expf(src[(long long)s * (R + 1) + R] - M);
+    for (int s = lane; s < k; s += kWave) Ls += expf(lses[s] - M);
     L = wave_sum(Ls);
-#pragma unroll 1
-    for (int s = 0; s < k; ++s) {
-      const float* row = src + (long long)s * (R + 1);
-      const float w = expf(row[R] - M);
+    // weights of partials c0 .. c0+63 live one per lane; a partial's weight
+    // is read from its lane
+    for (int c0 = 0; c0 < k; c0 += kWave) {
+      const float wl = c0 + lane < k ? expf(lses[c0 + lane] - M) : 0.0f;
+      const int ce = min(k, c0 + kWave);
+      for (int s0 = c0; s0 < ce; s0 += KC) {
+        if (s0 > 0) load_rows(s0);
 #pragma unroll
-      for (int j = 0; j < RJ; ++j) acc[j] = fmaf(w, row[lane + kWave * j], acc[j]);
+        for (int j = 0; j < KC; ++j) {
+          if (s0 + j < ce) {
+            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s0 + j - c0));
+#pragma unroll
+            for (int q = 0; q < V4; ++q) acc[q] += w * v[j][q];
+          }
+        }
+      }
     }
     const float inv = 1.0f / L;
 #pragma unroll
-    for (int j = 0; j < RJ; ++j) acc[j] *= inv;
+    for (int q = 0; q < V4; ++q) acc[q] *= inv;
   }
+  const long long bh = (long long)b * p.H + h;
 #pragma unroll
-  for (int j = 0; j < RJ; ++j) {
-    const long long idx = bh * R + lane + kWave * j;
-    if constexpr (QT == DT_F32) reinterpret_cast<float*>(p.o)[idx] = acc[j];
-    else reinterpret_cast<uint16_t*>(p.o)[idx] = (uint16_t)f32_to_bf16_rne(acc[j]);
+  for (int q = 0; q < V4; ++q) {
+    const long long idx = bh * R + 4 * (lane + kWave * q);
+    if constexpr (QT == DT_F32) {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + idx) = acc[q];
+    } else {
+      const uint32_t lo = f32_to_bf16_rne(acc[q][0]) | (f32_to_bf16_rne(acc[q][1]) << 16);
+      const uint32_t hi = f32_to_bf16_rne(acc[q][2]) | (f32_to_bf16_rne(acc[q][3]) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.o) + idx) = make_uint2(lo, hi);
+    }
   }
   if (lane == 0) p.lse[bh] = k > 0 ? M + logf(L) : -INFINITY;
 }

@@ -160,11 +160,23 @@ __device__ __forceinline__ int literal_num_partials(int n, int S) {
   return (n + kps - 1) / kps;
 }
 
-// Padded start of request b on the balanced line (every lane gets it).
-__device__ __forceinline__ long long balanced_start(const int32_t* __restrict__ seq_lens, int b, int lane) {
-  long long s = 0;
-  for (int i = lane; i < b; i += kWave) s += pad32(max(seq_lens[i], 0));
-  return wave_sum_i64(s);
+// The batch totals and request b's padded start from one pass over
+// seq_lens (one load per lane for up to 64 requests); every lane gets them.
+__device__ __forceinline__ BatchTotals batch_totals_and_start(const int32_t* __restrict__ seq_lens, int B, int b,
+                                                              int lane, long long& start) {
+  long long tot = 0, pre = 0;
+  int mx = 0;
+  for (int i = lane; i < B; i += kWave) {
+    const long long p = pad32(max(seq_lens[i], 0));
+    tot += p;
+    mx = max(mx, (int)p);
+    if (i < b) pre += p;
+  }
+  BatchTotals t;
+  t.total = wave_sum_i64(tot);
+  t.n32_max = wave_max_i32(mx);
+  start = wave_sum_i64(pre);
+  return t;
 }
 
 // ---------------------------------------------------------------------------
@@ -180,7 +192,7 @@ struct DecodeParams {
   long long bt_stride;
   const int32_t* seq_lens;
   const float* kv_scale;           // device scalar (fp8 cache) or null
-  float* ws;                       // [B, H, S, R + 1]
+  float* ws;                       // partial rows [B, H, S, R], then LSEs [B, H, S]
   void* o;                         // [B, H, R]
   float* lse;                      // [B, H]
   float sm_scale;
@@ -190,5 +202,16 @@ struct DecodeParams {
   int G;                           // balanced: chunk count
   int heads_per_group;             // stage 1: heads per workgroup
 };
+
+// Workspace layout (fp32, B*H*S*(R+1) values as the split workspace of the
+// pages): the normalised partial outputs as rows [B, H, S, R] -- each row a
+// multiple of 1 KB, so rows start on cache lines -- followed by their LSEs
+// [B, H, S].
+__device__ __forceinline__ float* ws_row(const DecodeParams& p, int b, int h, int s, int R) {
+  return p.ws + (((long long)b * p.H + h) * p.S + s) * R;
+}
+__device__ __forceinline__ float* ws_lse(const DecodeParams& p, int b, int h, int s, int R) {
+  return p.ws + (long long)p.B * p.H * p.S * R + ((long long)b * p.H + h) * p.S + s;
+}
 
 }  // namespace mla

@@ -19,7 +19,10 @@ struct WriteParams {
   int block_size;
   int R, P;
   const float* scale;
+  int tokens_per_wave;                  // write_tokens_per_wave(num_tokens)
 };
+
+int write_tokens_per_wave(long long num_tokens);
 
 hipError_t launch_cache_write(int in_dtype, int cache_dtype, const WriteParams& p, bool vec, hipStream_t stream);
 

@@ -22,7 +22,8 @@ Sources, cited by page and section (no line numbers):
   [API]   "vllm.v1.attention.backends.mla.triton_mla" API reference page.
   [OFP8]  OCP 8-bit Floating Point Specification (OFP8), E4M3 encoding.  The
           pages do not define the fp8 format; this is the published standard
-          the fp8 KV cache refers to (reading S5 in the design notes).
+          whose E4M3 flavour (largest finite value 448) matches a per-tensor
+          scale of amax / 448.
 
 Every function below is pinned by tests/test_oracle_*.py against closed forms,
 brute force, library routines (torch's fp8 cast, torch SDPA and logsumexp in
@@ -94,9 +95,9 @@ def fp8_e4m3fn_encode(x: np.ndarray) -> np.ndarray:
     """float32 -> E4M3 code by round-to-nearest, ties to the even code [OFP8].
 
     Finite magnitudes above the largest finite value 448 (and infinities)
-    saturate to +-448 (reading S6 in the design notes: the pages' conversion
-    helper is named but its body is not shown).  NaN maps to 0x7F with the input
-    sign.  The sign bit is always kept, so tiny negatives become 0x80.
+    saturate to +-448: the pages name the conversion helper but do not show
+    its body, and saturation is the reading taken here.  NaN maps to 0x7F with
+    the input sign.  The sign bit is always kept, so tiny negatives become 0x80.
 
     Written as a nearest-neighbour search over the 127 non-negative finite
     values, which is the definition of rounding, not a bit trick.
@@ -217,7 +218,8 @@ def attend(Q: np.ndarray, K: np.ndarray, R: int, sm_scale: float) -> Tuple[np.nd
     [ESSAY: Design motivation (single KV channel) and Data flow; DIFF:
     vllm/attention/backends/mla/utils.py, decode steps].  Returns o [H, R] and
     the natural-log LSE [H] of the scaled scores.  n == 0 gives o = 0 and
-    lse = -inf (reading S7).
+    lse = -inf (the pages would divide 0 by 0 there; this is the reading
+    taken).
     """
     H = Q.shape[0]
     n = K.shape[0]

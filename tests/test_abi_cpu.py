@@ -110,6 +110,8 @@ def test_decode_validation():
     for k in ["q", "cache", "bt", "seq", "ws", "o", "lse"]:
         assert _decode(**{k: None}) == -1, k
     assert _decode(ws=FAKE + 2) == -1               # misaligned workspace
+    assert _decode(ws=FAKE + 4) == -1               # workspace not 16-byte aligned
+    assert _decode(o=FAKE + 8) == -1                # output not 16-byte aligned
     assert _decode(wsb=4 * 128 * 4 * 513 * 4 - 4) == -3
     assert _decode(S=5) == -3                       # workspace sized for 4 splits
     assert _decode(B=0) == 0                        # empty batch: nothing launched
