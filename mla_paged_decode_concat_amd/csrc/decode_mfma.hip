@@ -49,6 +49,8 @@ namespace mla {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 #define MLA_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
 
@@ -177,15 +179,116 @@ struct TileLoad {
   }
 };
 
-template <int R, int NB, int NW, int STAGES>
+// fp8 E4M3 cache tiles.  A 32-token tile holds, per token quarter tq, the
+// value columns as R/128 full blocks (cq8, tq) of 8 tokens x 128 bytes at
+// (4 cq8 + tq) * 1024 (token t8, 16-byte chunk c8 at slot 8 t8 + c8), and
+// the 64 rope bytes as a half block at ROPE_OFF + tq * 512 (token t8, chunk y
+// at slot 4 t8 + y).  Loads of a full block are one LDS-DMA instruction
+// (each 8-lane group reads one 128-byte line); the rope half block is one
+// instruction with the upper 32 lanes masked off (their LDS destinations
+// would lie past the half block).  After the tile barrier the waves convert
+// the tile to the bf16 tile layout of TileLoad (fp8 -> fp32 -> bf16 is exact),
+// and the bf16 stage-1 code runs on that.
+template <int R, int NW>
+struct TileLoad8 {
+  static constexpr int D = R + 64;
+  static constexpr int FG = R / 128;                 // full 128-byte groups (the value columns)
+  static constexpr int NQ = 4 / NW;                  // token quarters per wave
+  static constexpr int LPW = NQ * (FG + 1);          // load instructions per wave per tile
+  static constexpr int ROPE_OFF = FG * 4096;
+  static constexpr int TILE_BYTES = ROPE_OFF + 4 * 512;
+  static constexpr int CPR = D / 16;                 // 16-byte chunks per row
+
+  struct Rows {
+    const char* full[NQ];
+    const char* rope[NQ];
+  };
+  static __device__ __forceinline__ const char* row_ptr(const DecodeParams& p, int tok, int se, int pg0,
+                                                        const int* s_table) {
+    tok = tok < se ? tok : se - 1;                 // past the range: re-read a valid row (masked later)
+    const int pg = tok / p.block_size;
+    const long long page = s_table[pg - pg0];
+    return reinterpret_cast<const char*>(p.cache) + page * p.block_stride + (long long)(tok - pg * p.block_size) * D;
+  }
+  static __device__ __forceinline__ Rows rows(const DecodeParams& p, int tile_start, int se, int pg0,
+                                              const int* s_table, int wave) {
+    const int lane = lane_now();
+    Rows rw;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int tq = wave + NW * j;
+      rw.full[j] = row_ptr(p, tile_start + 8 * tq + (lane >> 3), se, pg0, s_table) + (lane & 7) * 16;
+      rw.rope[j] = row_ptr(p, tile_start + 8 * tq + ((lane & 31) >> 2), se, pg0, s_table) + R + (lane & 3) * 16;
+    }
+    return rw;
+  }
+  template <int I>
+  static __device__ __forceinline__ void issue(const Rows& rw, const char* buf, int wave, int lane) {
+    constexpr int j = I / (FG + 1), k = I % (FG + 1);
+    const int tq = wave + NW * j;
+    if constexpr (k < FG) {
+      dma16<128 * k>(rw.full[j], lds_addr(buf) + (4 * k + tq) * 1024);
+    } else {
+      if (lane < 32) dma16<0>(rw.rope[j], lds_addr(buf) + ROPE_OFF + tq * 512);
+    }
+  }
+  static __device__ __forceinline__ void tile(const DecodeParams& p, int tile_start, int se, int pg0,
+                                              const char* buf, const int* s_table, int wave, int lane) {
+    const Rows rw = rows(p, tile_start, se, pg0, s_table, wave);
+    static_for<LPW>([&](auto i) { issue<decltype(i)::value>(rw, buf, wave, lane); });
+  }
+
+  // fp8 tile in `src` -> bf16 tile (TileLoad layout) in `dst`: this wave's quarters
+  static __device__ __forceinline__ void convert(const char* src, char* dst, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int tq = wave + NW * j;
+#pragma unroll
+      for (int it = 0; it < (8 * CPR + 63) / 64; ++it) {
+        const int id = lane + 64 * it;
+        if (id < 8 * CPR) {
+          const int t8 = id / CPR, c = id - t8 * CPR;
+          const char* from = c < 8 * FG ? src + (4 * (c >> 3) + tq) * 1024 + (8 * t8 + (c & 7)) * 16
+                                        : src + ROPE_OFF + tq * 512 + (4 * t8 + (c - 8 * FG)) * 16;
+          const u32x4_t w = *MLA_LDS(const u32x4_t, from);
+          const uint32_t wd[4] = {w[0], w[1], w[2], w[3]};
+          uint32_t o[8];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[q], false);   // bytes 0, 1
+            const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[q], true);    // bytes 2, 3
+            // upper halves of the fp32 values: exact bf16 (an E4M3 value has 4 significant bits)
+            o[2 * q] = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u);
+            o[2 * q + 1] = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u);
+          }
+          // 16 values = bf16 chunks 2c and 2c + 1
+          const int sw = TileLoad<R, NW>::swz(t8, tq);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int cb = 2 * c + h, cq8 = cb >> 3, c8 = cb & 7;
+            *MLA_LDS(u32x4_t, dst + (4 * cq8 + tq) * 1024 + (8 * t8 + (c8 ^ sw)) * 16) =
+                u32x4_t{o[4 * h], o[4 * h + 1], o[4 * h + 2], o[4 * h + 3]};
+          }
+        }
+      }
+    }
+  }
+};
+
+template <int R, int NB, int NW, int STAGES, bool F8 = false>
 struct Stage1 {
   using G = Geo<R>;
-  static constexpr int LPW = G::NBLK / NW;         // DMA instructions per wave per tile
+  using TL8 = TileLoad8<R, NW>;
+  // DMA instructions per wave per tile
+  static constexpr int LPW = F8 ? TL8::LPW : G::NBLK / NW;
   static_assert(G::NBLK % NW == 0, "tile blocks must split evenly over the waves");
   static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
   static constexpr int HPG = 16 * NB * NW;         // heads per workgroup
   static constexpr int NW_ = NW;
-  static constexpr int SMEM = STAGES * G::TILE_BYTES;
+  // ring slot per tile in flight; an fp8 cache adds one bf16 work tile
+  static constexpr int SLOT = F8 ? TL8::TILE_BYTES : G::TILE_BYTES;
+  static constexpr int WORK_OFF = STAGES * SLOT;
+  static constexpr int SMEM = STAGES * SLOT + (F8 ? G::TILE_BYTES : 0);
   static constexpr int TABLE = kTableWindow;       // block-table window staged in LDS
 
   // wait until the loads of the tile that has `after` newer tiles in flight landed
@@ -202,7 +305,10 @@ struct Stage1 {
   static __device__ __forceinline__ int swz(int t8, int tq) { return TileLoad<R, NW>::swz(t8, tq); }
   static __device__ __forceinline__ void issue_tile(const DecodeParams& p, int tile_start, int se, int pg0,
                                                     char* buf, const int* s_table, int wave, int lane) {
-    TileLoad<R, NW>::tile(p, tile_start, se, pg0, buf, buf + (G::CHUNKS / 8 - 1) * 4096, s_table, wave, lane);
+    if constexpr (F8)
+      TL8::tile(p, tile_start, se, pg0, buf, s_table, wave, lane);
+    else
+      TileLoad<R, NW>::tile(p, tile_start, se, pg0, buf, buf + (G::CHUNKS / 8 - 1) * 4096, s_table, wave, lane);
   }
 
   // Token range [a, e) of request b for this wave's heads; writes partial `part`.
@@ -214,6 +320,8 @@ struct Stage1 {
     const int r16 = lane & 15;
     head0 += wave * 16 * NB;                   // this wave's heads
 
+    // an fp8 cache stores row / kv_scale: the scale goes into the scores and the output
+    const float kvs = F8 ? *p.kv_scale : 1.0f;
     // ---- Q^T operand in registers: lane = head r16 of block nb, dims 32ks + 8g .. +8
     bf16x8_t qf[NB][G::KS];
     const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + (long long)b * p.q_sb;
@@ -230,10 +338,14 @@ struct Stage1 {
     wait_vmcnt<0>();
 
     f32x4_t acc[G::CB][NB];
-    float m_ref[NB], l_sum[NB], m_init[NB];
+    // l_sum: the exact sum of p (for the LSE); l_mma: the sum of p as rounded
+    // to bf16 for the matrix cores, which normalises acc.  The normalised
+    // weights then sum to one exactly, so the rounding of a dominant weight
+    // cancels instead of scaling the output by up to 2^-9.
+    float m_ref[NB], l_sum[NB], l_mma[NB], m_init[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) m_init[nb] = -INFINITY;
-    const float c2 = p.sm_scale * kLog2e;
+    const float c2 = p.sm_scale * kvs * kLog2e;
 
     // lane-constant LDS offsets
     // K rows (A operand of QK): token m = r16 of a 16-token block, chunk 4ks + g;
@@ -277,6 +389,7 @@ struct Stage1 {
       for (int nb = 0; nb < NB; ++nb) {
         m_ref[nb] = m_init[nb];
         l_sum[nb] = 0.0f;
+        l_mma[nb] = 0.0f;
       }
       bool redo = false;
 
@@ -297,7 +410,7 @@ struct Stage1 {
         const int ntiles = (se - sa + kTile - 1) / kTile;
 #pragma unroll
         for (int t = 0; t < STAGES - 1; ++t)
-          if (t < ntiles) issue_tile(p, sa + kTile * t, se, pg0, smem + t * G::TILE_BYTES, s_table, wave, lane);
+          if (t < ntiles) issue_tile(p, sa + kTile * t, se, pg0, smem + t * SLOT, s_table, wave, lane);
 
 #pragma unroll 1
         for (int t = 0; t < ntiles; ++t) {
@@ -310,9 +423,15 @@ struct Stage1 {
             break;
           }
           if (t + STAGES - 1 < ntiles)
-            issue_tile(p, sa + kTile * (t + STAGES - 1), se, pg0,
-                       smem + ((t + STAGES - 1) % STAGES) * G::TILE_BYTES, s_table, wave, lane);
-          const char* tile = smem + (t % STAGES) * G::TILE_BYTES;
+            issue_tile(p, sa + kTile * (t + STAGES - 1), se, pg0, smem + ((t + STAGES - 1) % STAGES) * SLOT,
+                       s_table, wave, lane);
+          const char* tile = smem + (t % STAGES) * SLOT;
+          if constexpr (F8) {
+            // every wave is past tile t-1's reads of the work tile (barrier above)
+            TL8::convert(tile, smem + WORK_OFF, wave, lane);
+            __syncthreads();   // the bf16 work tile is complete
+            tile = smem + WORK_OFF;
+          }
           const int tile_start = sa + kTile * t;
 
           // ---- S^T = K Q^T  (2 token blocks x NB head blocks); K rows read two
@@ -379,16 +498,19 @@ struct Stage1 {
           bf16x8_t pf[NB];
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
-            float ls = 0.0f;
+            float ls = 0.0f, lm = 0.0f;
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const float pj = __builtin_amdgcn_exp2f(s[mb][nb][i] - m_ref[nb]);
+                const __bf16 pb = (__bf16)pj;
                 ls += pj;
-                pf[nb][4 * mb + i] = (__bf16)pj;
+                lm += (float)pb;
+                pf[nb][4 * mb + i] = pb;
               }
             l_sum[nb] += ls;
+            l_mma[nb] += lm;
           }
 
           // ---- O^T += V^T P^T  (CB column blocks x NB head blocks); V^T read
@@ -426,10 +548,12 @@ struct Stage1 {
     // ---- finalize: l over the 4 lanes sharing a head, normalise, store the partial
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      float l = l_sum[nb];
+      float l = l_sum[nb], lm = l_mma[nb];
       l += __shfl_xor(l, 16, 64);
       l += __shfl_xor(l, 32, 64);
-      const float inv = 1.0f / l;
+      lm += __shfl_xor(lm, 16, 64);
+      lm += __shfl_xor(lm, 32, 64);
+      const float inv = kvs / lm;
       const float lse = (m_ref[nb] + __builtin_amdgcn_logf(l)) * kLn2;
       const int h = head0 + 16 * nb + r16;
       float* dst = ws_row(p, b, h, part, R);
@@ -535,7 +659,7 @@ __global__ __launch_bounds__(K::NW_ * 64) void stage1_mfma_kernel(DecodeParams p
 // ---------------------------------------------------------------------------
 
 bool mfma_supported(int H, int R, int cache_dtype) {
-  return cache_dtype == DT_BF16 && (R == 512 || R == 256) && H % 16 == 0;
+  return (cache_dtype == DT_BF16 || cache_dtype == DT_FP8) && (R == 512 || R == 256) && H % 16 == 0;
 }
 
 bool mfma_group_ok(int hpg) { return hpg == 16 || hpg == 32 || hpg == 64 || hpg == 128; }
@@ -552,9 +676,10 @@ int mfma_heads_per_group(int H, int S) {
 }
 
 // deepest pipeline whose wait count fits the 6-bit vmcnt field
-template <int R, int NW>
+template <int R, int NW, bool F8>
 constexpr int stages_for() {
-  return (2 * (Geo<R>::NBLK / NW) < 64) ? 4 : 3;
+  constexpr int lpw = F8 ? TileLoad8<R, NW>::LPW : Geo<R>::NBLK / NW;
+  return (2 * lpw < 64) ? 4 : 3;
 }
 
 template <class K>
@@ -566,20 +691,21 @@ static hipError_t launch_k(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int R>
+template <int R, bool F8>
 static hipError_t launch_r(const DecodeParams& p, hipStream_t stream) {
   switch (p.heads_per_group) {
-    case 128: return launch_k<Stage1<R, 2, 4, stages_for<R, 4>()>>(p, stream);
-    case 64: return launch_k<Stage1<R, 2, 2, stages_for<R, 2>()>>(p, stream);
-    case 32: return launch_k<Stage1<R, 2, 1, stages_for<R, 1>()>>(p, stream);
-    case 16: return launch_k<Stage1<R, 1, 1, stages_for<R, 1>()>>(p, stream);
+    case 128: return launch_k<Stage1<R, 2, 4, stages_for<R, 4, F8>(), F8>>(p, stream);
+    case 64: return launch_k<Stage1<R, 2, 2, stages_for<R, 2, F8>(), F8>>(p, stream);
+    case 32: return launch_k<Stage1<R, 2, 1, stages_for<R, 1, F8>(), F8>>(p, stream);
+    case 16: return launch_k<Stage1<R, 1, 1, stages_for<R, 1, F8>(), F8>>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_stage1_mfma(int cache_dtype, int R, const DecodeParams& p, hipStream_t stream) {
-  if (cache_dtype != DT_BF16) return hipErrorNotSupported;
-  return R == 512 ? launch_r<512>(p, stream) : launch_r<256>(p, stream);
+  if (cache_dtype == DT_BF16) return R == 512 ? launch_r<512, false>(p, stream) : launch_r<256, false>(p, stream);
+  if (cache_dtype == DT_FP8) return R == 512 ? launch_r<512, true>(p, stream) : launch_r<256, true>(p, stream);
+  return hipErrorNotSupported;
 }
 
 }  // namespace mla

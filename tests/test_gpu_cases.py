@@ -2,7 +2,7 @@
 against another GPU run where the property is exact):
 
 * every stage-1 kernel configuration (heads per workgroup 16/32/64/128),
-  both partitions, several grids;
+  both partitions, several grids, for a bf16 and an fp8 cache;
 * a late token whose score jumps far above the earlier maximum (the decode
   must redo the range with a larger softmax reference);
 * block sizes 1, 16, 48, 64 (1 exceeds the staged block-table window);
@@ -60,6 +60,21 @@ def test_mfma_head_groups_v3_shape(hpg, partition):
         compare(o, lse, o_ref, lse_ref, "bf16")
 
 
+@pytest.mark.parametrize("hpg", [16, 32, 64, 128])
+@pytest.mark.parametrize("partition", [1, 2])
+def test_mfma_head_groups_fp8_cache(hpg, partition):
+    """The matrix-core path with an fp8 cache (tiles converted to bf16 in LDS)."""
+    bt = W.make_batch(4, DEV, B=3, seq_lens=[1000, 777, 33])
+    ref_cache = oracle_cache(bt)
+    _write(bt)
+    assert np.array_equal(bt.cache.cpu().numpy(), ref_cache)
+    o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
+    for S in [1, 3, 16]:
+        _print(f"[mfma fp8] hpg={hpg} partition={partition} S={S}")
+        o, lse = _decode(bt, S, kernel=2, heads_per_group=hpg, partition=partition)
+        compare(o, lse, o_ref, lse_ref, "bf16")
+
+
 @pytest.mark.parametrize("grid", [1, 7, 64, 1000])
 def test_balanced_grid_sizes(grid):
     bt = W.make_batch(1, DEV, B=9, max_len=2500)
@@ -102,10 +117,11 @@ def test_late_dominant_token_forces_redo():
 
 
 @pytest.mark.parametrize("bs", [1, 16, 48, 64])
-def test_block_sizes(bs):
-    spec = W.SPECS[1]
+@pytest.mark.parametrize("index", [1, 4])
+def test_block_sizes(bs, index):
+    spec = W.SPECS[index]
     lens = [1, 31, 33, 1500, 2049]
-    bt = W.make_batch(1, DEV, seq_lens=lens)
+    bt = W.make_batch(index, DEV, seq_lens=lens, H=16)
     # rebuild the paging with block size bs over the same token rows
     nblk = [-(-n // bs) for n in lens]
     g = torch.Generator().manual_seed(bs)
@@ -120,11 +136,16 @@ def test_block_sizes(bs):
         slots.append(ids[j // bs] * bs + j % bs)
     bt.block_table = table.to(DEV)
     bt.slot_mapping = torch.cat(slots).to(DEV)
-    bt.cache = torch.full((sum(nblk) + 1, bs, spec.D), W.NAN_BF16, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    if spec.cache_dtype == "fp8":
+        bt.cache = torch.full((sum(nblk) + 1, bs, spec.D), W.NAN_FP8, dtype=torch.uint8, device=DEV)
+    else:
+        bt.cache = torch.full((sum(nblk) + 1, bs, spec.D), W.NAN_BF16, dtype=torch.int16,
+                              device=DEV).view(torch.bfloat16)
+    scale = float(bt.scale[0].cpu()) if bt.scale is not None else None
     ref_cache = O.cache_write(W.bits(bt.cache), W.bits(bt.kv_c), W.bits(bt.k_pe), bt.slot_mapping.cpu().numpy(),
-                              "bf16", "bf16")
+                              "bf16", spec.cache_dtype, scale)
     _write(bt)
-    assert np.array_equal(bt.cache.cpu().view(torch.int16).numpy().view(np.uint16), ref_cache)
+    assert np.array_equal(W.bits(bt.cache), ref_cache)
     o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
     for S in [1, 4]:
         for kernel in [1, 2]:
