@@ -303,6 +303,48 @@ def merge(parts: Sequence[Tuple[np.ndarray, np.ndarray]]) -> Tuple[np.ndarray, n
     return o, M + np.log(tot)
 
 
+def decode_multi_token(q: np.ndarray, cache: np.ndarray, block_table: np.ndarray,
+                       seq_lens: np.ndarray, sm_scale: float, q_dtype: str, cache_dtype: str,
+                       kv_lora_rank: int, kv_scale: float | None = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Non-causal multi-token decode: q [B, T, H, D] holds T query tokens per
+    request, each attending to all of the request's cached tokens.  As the
+    pages do it, every query token becomes a decode row of its own that
+    carries its request's block table and length [API:
+    TritonMLAMetadataBuilder, non-causal multi-token decode]; then ``decode``.
+    Returns o [B, T, H, R] and lse [B, T, H]."""
+    B, T, H, D = q.shape
+    rows = np.asarray(q).reshape(B * T, H, D)
+    table = np.repeat(np.asarray(block_table), T, axis=0)
+    lens = np.repeat(np.asarray(seq_lens), T)
+    o, lse = decode(rows, cache, table, lens, sm_scale, q_dtype, cache_dtype, kv_lora_rank, kv_scale)
+    return o.reshape(B, T, H, kv_lora_rank), lse.reshape(B, T, H)
+
+
+def merge_shards(o_parts: np.ndarray, lse_parts: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Combine the results of G shards that attended to disjoint key sets of
+    the same queries (decode context parallelism: each GPU holds part of a
+    request's tokens and every head) [ESSAY: Design motivation (the LSE is
+    returned for the cross-shard merge); API: DCP gathers all query heads].
+
+    o_parts [G, B, H, R], lse_parts [G, B, H] (natural log).  Per (b, h) it is
+    the same LSE-weighted mean as ``merge``; shards with lse = -inf hold no
+    keys and get weight 0.  When every shard is empty the result is o = 0 and
+    lse = -inf, the empty-request reading of ``attend``.
+    """
+    Op = np.asarray(o_parts, dtype=np.float64)
+    L = np.asarray(lse_parts, dtype=np.float64)
+    G, B, H = L.shape
+    o = np.zeros(Op.shape[1:])
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            live = [g for g in range(G) if L[g, b, h] != -np.inf]
+            if live:
+                ob, lb = merge([(Op[g, b, h][None], L[g, b, h][None]) for g in live])
+                o[b, h], lse[b, h] = ob[0], lb[0]
+    return o, lse
+
+
 def decode_split_merge(q: np.ndarray, cache: np.ndarray, block_table: np.ndarray,
                        seq_lens: np.ndarray, sm_scale: float, q_dtype: str,
                        cache_dtype: str, kv_lora_rank: int, num_splits: int,

@@ -274,3 +274,80 @@ def test_fp32_arithmetic_stays_inside_tolerance():
     o32 = (e / e.sum(axis=1, keepdims=True)) @ K32[:, :512]
     assert np.max(np.abs(o32 - o)) < 1e-5 / 10
     assert np.max(np.abs(l32 - lse)) < 1e-5 / 10
+
+
+def _torch_attention(Q, K, R, sm):
+    """Softmax attention over all rows with torch in float64 (a library pin,
+    independent of the oracle's arithmetic)."""
+    s = sm * (torch.from_numpy(Q) @ torch.from_numpy(K).T)
+    lse = torch.logsumexp(s, dim=1)
+    o = torch.softmax(s, dim=1) @ torch.from_numpy(K[:, :R])
+    return o.numpy(), lse.numpy()
+
+
+@pytest.mark.parametrize("G", [1, 2, 5])
+def test_merge_shards_equals_attention_over_all_keys(G):
+    rng = np.random.default_rng(40 + G)
+    B, H, R, sm = 3, 4, 512, 0.06
+    lens = [37, 1, 200]
+    o_parts = np.zeros((G, B, H, R))
+    lse_parts = np.zeros((G, B, H))
+    want_o = np.zeros((B, H, R))
+    want_l = np.zeros((B, H))
+    for b, n in enumerate(lens):
+        Q, K = _rand_case(rng, n, H=H)
+        owner = rng.integers(0, G, size=n)       # any disjoint split of the rows
+        if G > 1:
+            owner[owner == G - 1] = 0            # shard G-1 holds no rows
+        for g in range(G):
+            o_parts[g, b], lse_parts[g, b] = O.attend(Q, K[owner == g], R, sm)
+        want_o[b], want_l[b] = _torch_attention(Q, K, R, sm)
+    o, lse = O.merge_shards(o_parts, lse_parts)
+    assert np.max(np.abs(o - want_o)) < 1e-12
+    assert np.max(np.abs(lse - want_l)) < 1e-12
+    perm = rng.permutation(G)                    # shard order does not matter
+    o2, l2 = O.merge_shards(o_parts[perm], lse_parts[perm])
+    assert np.max(np.abs(o2 - o)) < 1e-12 and np.max(np.abs(l2 - lse)) < 1e-12
+
+
+def test_merge_shards_empty_and_single():
+    rng = np.random.default_rng(3)
+    o_parts = rng.standard_normal((3, 2, 2, 256))
+    lse_parts = np.full((3, 2, 2), -np.inf)
+    lse_parts[1, 0, 1] = 2.5                     # one live shard for (0, 1)
+    o, lse = O.merge_shards(o_parts, lse_parts)
+    assert np.array_equal(o[0, 1], o_parts[1, 0, 1]) and lse[0, 1] == 2.5
+    for b, h in [(0, 0), (1, 0), (1, 1)]:        # every shard empty
+        assert lse[b, h] == -np.inf and not np.any(o[b, h])
+    # two shards with equal LSE: the plain mean, and lse + ln 2
+    lse_parts[:, 1, 1] = [0.5, 0.5, -np.inf]
+    o, lse = O.merge_shards(o_parts, lse_parts)
+    assert np.max(np.abs(o[1, 1] - 0.5 * (o_parts[0, 1, 1] + o_parts[1, 1, 1]))) < 1e-15
+    assert abs(lse[1, 1] - (0.5 + math.log(2.0))) < 1e-15
+
+
+def test_decode_multi_token_rows_attend_to_whole_sequence():
+    """Every query token of a non-causal block sees all of its request's
+    tokens: each (b, t) row against torch attention over the rows gathered
+    by hand from the paged cache; a block of one token is plain decode."""
+    rng = np.random.default_rng(21)
+    B, T, H, R, P, bs = 3, 3, 2, 512, 64, 4
+    lens = np.array([9, 1, 0])
+    cache = rng.standard_normal((8, bs, R + P)).astype(np.float32)
+    table = np.array([[5, 0, 7], [2, 2, 2], [1, 1, 1]], dtype=np.int32)
+    q = rng.standard_normal((B, T, H, R + P)).astype(np.float32)
+    sm = 0.05
+    o, lse = O.decode_multi_token(q, cache, table, lens, sm, "f32", "f32", R)
+    assert o.shape == (B, T, H, R) and lse.shape == (B, T, H)
+    for b in range(B):
+        K = np.array([cache[table[b, j // bs], j % bs] for j in range(lens[b])], dtype=np.float64)
+        for t in range(T):
+            if lens[b] == 0:
+                assert np.all(lse[b, t] == -np.inf) and not np.any(o[b, t])
+                continue
+            want_o, want_l = _torch_attention(q[b, t].astype(np.float64), K, R, sm)
+            assert np.max(np.abs(o[b, t] - want_o)) < 1e-12
+            assert np.max(np.abs(lse[b, t] - want_l)) < 1e-12
+    o1, l1 = O.decode_multi_token(q[:, :1], cache, table, lens, sm, "f32", "f32", R)
+    o0, l0 = O.decode(q[:, 0], cache, table, lens, sm, "f32", "f32", R)
+    assert np.array_equal(o1[:, 0], o0) and np.array_equal(l1[:, 0], l0)
