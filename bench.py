@@ -107,6 +107,8 @@ def parse():
     ap.add_argument("--heads-per-group", type=int, default=0)
     ap.add_argument("--partition", type=int, default=0)
     ap.add_argument("--no-invariant", action="store_true", help="skip the num_kv_splits=1 timing")
+    ap.add_argument("--main-only", action="store_true",
+                    help="run only the warmup and timed step loop (profiler runs: every decode launch is a step's)")
     return ap.parse_args()
 
 
@@ -174,10 +176,25 @@ def main():
     st2 = [e[1].ms_until(e[2]) for e in evs]
     st1_ms = statistics.mean(st1)
     st2_ms = statistics.mean(st2)
+    dec_us = sorted((a + b) * 1e3 for a, b in zip(st1, st2))
+
+    # decode with the 256 MB last-level cache flushed before every step (a
+    # 512 MB write outside the timed region), per-step events
+    fl_us = None
+    if not args.main_only:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        n_fl = max(5, K // 2)
+        evf = [[HipEvent() for _ in range(3)] for _ in range(n_fl)]
+        for k in range(n_fl):
+            flush.fill_(k & 0xFF)
+            step(S, evf[k])
+        torch.cuda.synchronize()
+        fl_us = sorted((e[0].ms_until(e[1]) + e[1].ms_until(e[2])) * 1e3 for e in evf)
+        del flush
 
     # batch-invariant run: one split per request
     inv_us = None
-    if not args.no_invariant:
+    if not (args.no_invariant or args.main_only):
         ws1 = torch.empty(M.decode_workspace_bytes(B, H, 1, R) // 4, dtype=torch.float32, device=dev)
         for _ in range(3):
             M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, W.SM_SCALE, 1, R, workspace=ws1, o=o, lse=lse, **kw)
@@ -189,6 +206,48 @@ def main():
             M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, W.SM_SCALE, 1, R, workspace=ws1, o=o, lse=lse, **kw)
         torch.cuda.synchronize()
         inv_us = (time.perf_counter() - ta) * 1e6 / n_inv
+
+    extras = None
+    if not args.main_only:
+        # the rows beyond the single-token step, each timed on its own with events
+        def timed_us(fn, n=10):
+            for _ in range(3):
+                fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(n):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / n
+
+        # non-causal multi-token decode: 2 query tokens per request on the same
+        # cache, run as 2*H rows of one request
+        q2 = W.multi_token_q(bt, 2)
+        S2 = S
+        ws2 = torch.empty(M.decode_workspace_bytes(B, 2 * H, S2, R) // 4, dtype=torch.float32, device=dev)
+        o2 = torch.empty((B, 2, H, R), dtype=torch.bfloat16, device=dev)
+        lse2 = torch.empty((B, 2, H), dtype=torch.float32, device=dev)
+        mtok_us = timed_us(lambda: M.decode(q2, bt.cache, bt.block_table, bt.seq_lens, W.SM_SCALE, S2, R,
+                                            workspace=ws2, o=o2, lse=lse2))
+        dec1_us = timed_us(lambda: M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, W.SM_SCALE, S, R,
+                                            workspace=ws, o=o, lse=lse))
+        del q2, ws2, o2, lse2
+        # merge of 8 shard results of this batch's shape (bf16 o, fp32 lse)
+        G8 = 8
+        o_parts = torch.randn((G8, B, H, R), device=dev).to(torch.bfloat16)
+        lse_parts = torch.randn((G8, B, H), device=dev)
+        om = torch.empty((B, H, R), dtype=torch.bfloat16, device=dev)
+        lm = torch.empty((B, H), dtype=torch.float32, device=dev)
+        merge_us = timed_us(lambda: M.merge_partials(o_parts, lse_parts, om, lm), n=20)
+        merge_bytes = G8 * B * H * (R * 2 + 4) + B * H * (R * 2 + 4)
+        del o_parts, lse_parts
+        extras = {
+            "decode_us_q_len1": round(dec1_us, 2),
+            "decode_us_q_len2_noncausal": round(mtok_us, 2),
+            "shard_merge_g8_us": round(merge_us, 2),
+            "shard_merge_g8_gbps": round(merge_bytes / (merge_us * 1e-6) / 1e9, 1),
+        }
 
     if args.copy_probe_mb:
         src = torch.empty(args.copy_probe_mb * (1 << 20) // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -250,9 +309,39 @@ def main():
         "hbm_floor_us": round(kv_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
         "bulk_write_gbps": round(bulk_gbs, 1),
         "batch_invariant_us_per_step": round(inv_us, 2) if inv_us else None,
+        "decode_us_p10_p50_p90": [round(pct(dec_us, q), 2) for q in (10, 50, 90)],
+        "decode_us_llc_flushed_p10_p50_p90": [round(pct(fl_us, q), 2) for q in (10, 50, 90)] if fl_us else None,
+        "num_kv_splits_effective": effective_splits(bt.seq_lens_list, S, cus),
+        "beyond_single_token": extras,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def pct(sorted_vals, q):
+    """q-th percentile (nearest rank) of an ascending list."""
+    i = min(len(sorted_vals) - 1, max(0, int(math.ceil(q / 100.0 * len(sorted_vals))) - 1))
+    return sorted_vals[i]
+
+
+def effective_splits(lens, S, cus):
+    """Most partials any request gets from the library's balanced partition
+    with the MFMA kernel's default grid (one chunk per CU; the rule is stated
+    with the library's split-partition code): requests padded to 32 tokens are
+    laid end to end and cut into G chunks of Q tokens, Q a multiple of 32 and
+    at least ceil(n32_max / (S - 1))."""
+    if S == 1:
+        return 1
+    pad = [-(-n // 32) * 32 for n in lens]
+    total, n32max, G = sum(pad), max(pad), cus
+    Q = max(-(-total // G), -(-n32max // (S - 1)))
+    Q = max(32, -(-Q // 32) * 32)
+    start, most = 0, 0
+    for n, p in zip(lens, pad):
+        if n > 0:
+            most = max(most, (start + n - 1) // Q - start // Q + 1)
+        start += p
+    return most
 
 
 def cpu_baseline(bt, step_kv_c, step_k_pe, step_slots, seconds):

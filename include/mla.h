@@ -52,6 +52,29 @@ enum {
 };
 
 /* Human-readable text for a status code (static storage). */
+/*
+ * Merge of partial attention results over disjoint key sets: combining the
+ * per-shard outputs of a request whose tokens are split across GPUs (decode
+ * context parallelism), here on one GPU's buffers.  For every (b, h):
+ *   M = max_g lse_g,   w_g = exp(lse_g - M),
+ *   o[b][h][:] = sum_g w_g o_g[b][h][:] / sum_g w_g,   lse[b][h] = M + ln sum_g w_g,
+ * the same LSE merge as decode stage 2.  A shard with lse_g = -inf (no keys)
+ * contributes nothing; if every shard is empty, o = 0 and lse = -inf.
+ * [ESSAY: Design motivation (the decode returns the LSE because the
+ *  cross-shard merge relies on it; natural-log LSE); API: DCP all-gathers the
+ *  query heads before forward_mqa, so each shard holds every head]
+ *   o_parts   : [G, B, H, R] contiguous, element type `dtype`, 16-byte aligned
+ *   lse_parts : [G, B, H] contiguous fp32, natural log
+ *   dtype     : MLA_F32 or MLA_BF16 (o_parts and o); accumulation is fp32
+ *   o         : [B, H, R] contiguous, element type `dtype`, 16-byte aligned
+ *   lse       : [B, H] contiguous fp32
+ *   R         : 512 or 256
+ * Errors: MLA_ERR_ARG (G < 1, B < 0, H < 1, a NULL pointer, misalignment),
+ * MLA_ERR_UNSUPPORTED (R, dtype), MLA_ERR_HIP.  B == 0 launches nothing.
+ */
+int mla_merge_partials(const void* o_parts, const float* lse_parts, int G, int B, int H, int R, int dtype,
+                       void* o, float* lse, void* stream);
+
 const char* mla_status_string(int status);
 
 /*
@@ -131,6 +154,16 @@ int mla_cache_write(const void* kv_c, int64_t kv_c_row_stride,
  * and returns o[b][h][:] = sum_j softmax_j(s_h) * r_j[0 : R)  (dtype q_dtype)
  * and lse[b][h] = ln sum_j exp(s_hj)  (fp32, natural log, includes sm_scale).
  * n == 0 gives o = 0 and lse = -inf.
+ *
+ * Multi-token rows.  A request whose q_len query tokens all attend, with no
+ * causal mask among them, to the same n cached tokens (a non-causal
+ * speculative block, which the pages flatten to one decode row per query
+ * token [API: TritonMLAMetadataBuilder, non-causal multi-token decode]) is
+ * passed as H = q_len * heads rows: q [B, q_len, heads, R + P] with
+ * q_stride_h the head stride and a token stride of heads * q_stride_h; o and
+ * lse then read as [B, q_len, heads, R] and [B, q_len, heads].  The rows of a
+ * request are processed together, so each KV tile is read once for all of
+ * them rather than once per query token.
  *
  * Two stages run on `stream`: stage 1 writes per-split normalised partial
  * outputs and LSEs into `workspace` (fp32; layout at

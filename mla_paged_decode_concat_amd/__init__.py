@@ -12,5 +12,6 @@ from .binding import (  # noqa: F401
     decode_workspace_bytes,
     library_path,
     load_library,
+    merge_partials,
     num_kv_splits,
 )

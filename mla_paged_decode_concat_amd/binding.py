@@ -20,7 +20,7 @@ MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace too small", -4: "HIP failure"}
 
 EXPORTS = ["mla_status_string", "mla_num_kv_splits", "mla_decode_workspace_bytes", "mla_cache_write",
-           "mla_decode", "mla_decode_ex"]
+           "mla_decode", "mla_decode_ex", "mla_merge_partials"]
 
 
 class MLAError(RuntimeError):
@@ -67,6 +67,8 @@ def load_library():
     lib.mla_decode.argtypes = dec
     lib.mla_decode_ex.restype = i32
     lib.mla_decode_ex.argtypes = dec + [ctypes.POINTER(DecodeOpts)]
+    lib.mla_merge_partials.restype = i32
+    lib.mla_merge_partials.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -83,6 +85,19 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 def _stream(dev: torch.device) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _same_gpu(*tensors: Optional[torch.Tensor]) -> None:
+    """The library takes device pointers: every tensor must live on one GPU."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"tensor on {t.device}: the library takes GPU tensors only")
+        if dev is not None and t.device != dev:
+            raise ValueError(f"tensors on {dev} and {t.device}")
+        dev = t.device
 
 
 def _check(status: int, what: str) -> None:
@@ -118,6 +133,13 @@ def cache_write(kv_c: torch.Tensor, k_pe: torch.Tensor, kv_cache: torch.Tensor, 
         raise ValueError("rows must be contiguous")
     if not slot_mapping.is_contiguous():
         raise ValueError("slot_mapping must be contiguous")
+    if k_pe.shape[0] != kv_c.shape[0] or slot_mapping.numel() > kv_c.shape[0]:
+        raise ValueError("kv_c and k_pe need one row per slot_mapping entry")
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != kv_c.shape[1] + k_pe.shape[1]:
+        raise ValueError("kv_cache must be [num_blocks, block_size, R + P]")
+    if scale is not None and scale.numel() < 1:
+        raise ValueError("scale must hold one fp32 value")
+    _same_gpu(kv_c, k_pe, kv_cache, slot_mapping, scale)
     st = load_library().mla_cache_write(
         kv_c.data_ptr(), kv_c.stride(0), k_pe.data_ptr(), k_pe.stride(0), in_dt,
         slot_mapping.data_ptr(), slot_mapping.numel(),
@@ -134,9 +156,24 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
            partition: int = 0, kernel: int = 0, grid: int = 0, heads_per_group: int = 0,
            stage_events=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """MLA decode of q [B, H, R+P] against the paged latent cache.  Returns
-    o [B, H, R] (q's dtype) and the natural-log lse [B, H] (fp32)."""
+    o [B, H, R] (q's dtype) and the natural-log lse [B, H] (fp32).
+
+    q may also be [B, q_len, H, R+P]: q_len query tokens per request that all
+    attend to the request's whole cached sequence (non-causal multi-token
+    decode); they run as q_len * H rows of one request, and o and lse come
+    back as [B, q_len, H, R] and [B, q_len, H]."""
     if isinstance(q, tuple):
         q = torch.cat(q, dim=-1)
+    if q.dim() == 4:
+        B, T, H, D = q.shape
+        if q.stride(1) != H * q.stride(2):
+            raise ValueError("a [B, q_len, H, D] query needs token stride H * head stride")
+        flat = torch.as_strided(q, (B, T * H, D), (q.stride(0), q.stride(2), q.stride(3)))
+        o_flat = o.view(B, T * H, -1) if o is not None else None
+        lse_flat = lse.view(B, T * H) if lse is not None else None
+        of, lf = decode(flat, kv_cache, block_table, seq_lens, sm_scale, num_kv_splits, kv_lora_rank, kv_scale,
+                        workspace, o_flat, lse_flat, partition, kernel, grid, heads_per_group, stage_events)
+        return of.view(B, T, H, -1), lf.view(B, T, H)
     B, H, D = q.shape
     R = kv_lora_rank
     P = D - R
@@ -146,6 +183,12 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
         raise TypeError("block_table and seq_lens must be int32 (seq_lens contiguous)")
     if block_table.stride(-1) != 1:
         raise ValueError("block_table rows must be contiguous")
+    if seq_lens.numel() != B or block_table.dim() != 2 or block_table.shape[0] < B:
+        raise ValueError("seq_lens must hold B entries and block_table B rows")
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != D:
+        raise ValueError("kv_cache must be [num_blocks, block_size, R + P]")
+    if kv_scale is not None and kv_scale.numel() < 1:
+        raise ValueError("kv_scale must hold one fp32 value")
     lib = load_library()
     if o is None:
         o = torch.empty((B, H, R), dtype=q.dtype, device=q.device)
@@ -156,6 +199,9 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
         workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=q.device)
     if not (o.is_contiguous() and lse.is_contiguous() and lse.dtype == torch.float32 and o.dtype == q.dtype):
         raise ValueError("o must be contiguous in q's dtype and lse contiguous fp32")
+    if tuple(o.shape) != (B, H, R) or tuple(lse.shape) != (B, H):
+        raise ValueError("o must be [B, H, R] and lse [B, H]")
+    _same_gpu(q, kv_cache, block_table, seq_lens, kv_scale, workspace, o, lse)
     opts = DecodeOpts(partition, kernel, grid, heads_per_group)
     if stage_events is not None:   # three torch.cuda.Event (or None) recorded around the two stages
         for i, ev in enumerate(stage_events):
@@ -168,4 +214,29 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), o.data_ptr(), lse.data_ptr(),
         _stream(q.device), ctypes.byref(opts))
     _check(st, "mla_decode")
+    return o, lse
+
+
+def merge_partials(o_parts: torch.Tensor, lse_parts: torch.Tensor, o: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Merge G shard results o_parts [G, B, H, R] (fp32 or bf16) with their
+    natural-log LSEs lse_parts [G, B, H] into o [B, H, R] and lse [B, H]."""
+    G, B, H, R = o_parts.shape
+    if tuple(lse_parts.shape) != (G, B, H) or lse_parts.dtype != torch.float32:
+        raise ValueError("lse_parts must be fp32 [G, B, H]")
+    if not (o_parts.is_contiguous() and lse_parts.is_contiguous()):
+        raise ValueError("o_parts and lse_parts must be contiguous")
+    if o is None:
+        o = torch.empty((B, H, R), dtype=o_parts.dtype, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=o_parts.device)
+    if not (o.is_contiguous() and lse.is_contiguous() and o.dtype == o_parts.dtype and lse.dtype == torch.float32):
+        raise ValueError("o must be contiguous in o_parts' dtype and lse contiguous fp32")
+    if tuple(o.shape) != (B, H, R) or tuple(lse.shape) != (B, H):
+        raise ValueError("o must be [B, H, R] and lse [B, H]")
+    _same_gpu(o_parts, lse_parts, o, lse)
+    st = load_library().mla_merge_partials(o_parts.data_ptr(), lse_parts.data_ptr(), G, B, H, R,
+                                           _dtype_code(o_parts), o.data_ptr(), lse.data_ptr(),
+                                           _stream(o_parts.device))
+    _check(st, "mla_merge_partials")
     return o, lse

@@ -210,6 +210,22 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
   return MLA_OK;
 }
 
+int mla_merge_partials(const void* o_parts, const float* lse_parts, int G, int B, int H, int R, int dtype,
+                       void* o, float* lse, void* stream) {
+  if (R != 512 && R != 256) return MLA_ERR_UNSUPPORTED;
+  if (dtype != MLA_F32 && dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (G < 1 || B < 0 || H < 1) return MLA_ERR_ARG;
+  if (B == 0) return MLA_OK;
+  if (!o_parts || !lse_parts || !o || !lse) return MLA_ERR_ARG;
+  if (!aligned16(o_parts) || !aligned16(o) || reinterpret_cast<uintptr_t>(lse_parts) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(lse) % 4 != 0)
+    return MLA_ERR_ARG;
+  (void)hipGetLastError();
+  const hipError_t e = launch_shard_merge(dtype, R, o_parts, lse_parts, G, (long long)B * H, o, lse,
+                                          reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 int mla_decode(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_dtype,
                int B, int H,
                const void* cache, int cache_dtype, int64_t num_blocks, int block_size,

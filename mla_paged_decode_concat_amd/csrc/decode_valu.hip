@@ -277,6 +277,80 @@ __global__ __launch_bounds__(kWave * kMergeWaves) void stage2_merge_kernel(Decod
   if (lane == 0) p.lse[bh] = k > 0 ? M + logf(L) : -INFINITY;
 }
 
+// ---------------------------------------------------------------------------
+// Merge of G shard results (o_g, lse_g) of the same queries: one wave per
+// (request, head), 4 per workgroup; the weights are those of stage 2.
+// ---------------------------------------------------------------------------
+template <int DT, int R>
+__global__ __launch_bounds__(kWave * kMergeWaves) void shard_merge_kernel(const void* __restrict__ o_parts,
+                                                                          const float* __restrict__ lse_parts,
+                                                                          int G, long long BH, void* o,
+                                                                          float* lse) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  constexpr int V4 = R / (4 * kWave);   // 4-element groups per lane per row
+  const int lane = threadIdx.x & (kWave - 1);
+  const long long bh = (long long)blockIdx.x * kMergeWaves + threadIdx.x / kWave;
+  if (bh >= BH) return;
+  float M = -INFINITY;
+  for (int g = lane; g < G; g += kWave) M = fmaxf(M, lse_parts[g * BH + bh]);
+  M = wave_max(M);
+  f32x4 acc[V4];
+#pragma unroll
+  for (int q = 0; q < V4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float L = 0.0f;
+  if (M != -INFINITY) {
+    float Ls = 0.0f;
+    for (int g = lane; g < G; g += kWave) Ls += expf(lse_parts[g * BH + bh] - M);
+    L = wave_sum(Ls);
+#pragma unroll 4
+    for (int g = 0; g < G; ++g) {
+      const float w = expf(lse_parts[g * BH + bh] - M);   // 0 for an empty shard
+      const long long row = (g * BH + bh) * R;
+#pragma unroll
+      for (int q = 0; q < V4; ++q) {
+        const long long idx = row + 4 * (lane + kWave * q);
+        f32x4 v;
+        if constexpr (DT == DT_F32) {
+          v = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(o_parts) + idx);
+        } else {
+          const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(o_parts) + idx);
+          v = f32x4{bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffffu),
+                    bf16_to_f32(u.y >> 16)};
+        }
+        acc[q] += w * v;
+      }
+    }
+    const float inv = 1.0f / L;
+#pragma unroll
+    for (int q = 0; q < V4; ++q) acc[q] *= inv;
+  }
+#pragma unroll
+  for (int q = 0; q < V4; ++q) {
+    const long long idx = bh * R + 4 * (lane + kWave * q);
+    if constexpr (DT == DT_F32) {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + idx) = acc[q];
+    } else {
+      const uint32_t lo = f32_to_bf16_rne(acc[q][0]) | (f32_to_bf16_rne(acc[q][1]) << 16);
+      const uint32_t hi = f32_to_bf16_rne(acc[q][2]) | (f32_to_bf16_rne(acc[q][3]) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(o) + idx) = make_uint2(lo, hi);
+    }
+  }
+  if (lane == 0) lse[bh] = M != -INFINITY ? M + logf(L) : -INFINITY;
+}
+
+hipError_t launch_shard_merge(int dtype, int R, const void* o_parts, const float* lse_parts, int G, long long BH,
+                              void* o, float* lse, hipStream_t stream) {
+  dim3 grid((unsigned)((BH + kMergeWaves - 1) / kMergeWaves)), block(kWave * kMergeWaves);
+  if (dtype == DT_F32) {
+    if (R == 512) hipLaunchKernelGGL((shard_merge_kernel<DT_F32, 512>), grid, block, 0, stream, o_parts, lse_parts, G, BH, o, lse);
+    else hipLaunchKernelGGL((shard_merge_kernel<DT_F32, 256>), grid, block, 0, stream, o_parts, lse_parts, G, BH, o, lse);
+  } else {
+    if (R == 512) hipLaunchKernelGGL((shard_merge_kernel<DT_BF16, 512>), grid, block, 0, stream, o_parts, lse_parts, G, BH, o, lse);
+    else hipLaunchKernelGGL((shard_merge_kernel<DT_BF16, 256>), grid, block, 0, stream, o_parts, lse_parts, G, BH, o, lse);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_stage2(int q_dtype, int R, const DecodeParams& p, hipStream_t stream) {
   const int hblocks = (p.H + kMergeWaves - 1) / kMergeWaves;
   dim3 grid((unsigned)(p.B * hblocks)), block(kWave * kMergeWaves);

@@ -29,6 +29,8 @@ hipError_t launch_cache_write(int in_dtype, int cache_dtype, const WriteParams& 
 hipError_t launch_stage1_valu(int q_dtype, int cache_dtype, int R, const DecodeParams& p, hipStream_t stream);
 hipError_t launch_stage1_mfma(int cache_dtype, int R, const DecodeParams& p, hipStream_t stream);
 hipError_t launch_stage2(int q_dtype, int R, const DecodeParams& p, hipStream_t stream);
+hipError_t launch_shard_merge(int dtype, int R, const void* o_parts, const float* lse_parts, int G, long long BH,
+                              void* o, float* lse, hipStream_t stream);
 
 // Stage-1 MFMA kernel geometry, needed by the host planner.
 int mfma_heads_per_group(int H, int S);

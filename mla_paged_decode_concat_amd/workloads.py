@@ -209,3 +209,15 @@ def bits(t: torch.Tensor):
     if t.dtype == torch.float8_e4m3fn:
         return t.view(torch.uint8).numpy()
     return t.numpy()
+
+
+def multi_token_q(bt: Batch, q_len: int, seed: Optional[int] = None) -> torch.Tensor:
+    """Query block of ``q_len`` tokens per request, [B, q_len, H, R+P], drawn
+    like the batch's q: N(0, 1) float32 on a generator on the batch's device
+    (seeded 2000 + workload index unless given), cast to the input dtype."""
+    spec = bt.spec
+    dev = bt.q.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(2000 + spec.index if seed is None else seed)
+    shape = (bt.B, q_len, spec.H, spec.D)
+    return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch_dtype(spec.in_dtype))

@@ -124,3 +124,47 @@ def test_decode_ex_validation():
     assert _decode(O_(0, 0, -1, 0)) == -1
     assert _decode(O_(0, 2, 0, 0), q_dt=0, cache_dt=0) == -2   # MFMA kernel needs a bf16 query
     assert _decode(O_(0, 0, 0, 0), B=0) == 0
+
+
+def _merge(**kw):
+    a = dict(o_parts=FAKE, lse_parts=FAKE, G=4, B=8, H=16, R=512, dt=1, o=FAKE, lse=FAKE, stream=None)
+    a.update(kw)
+    return binding.load_library().mla_merge_partials(*a.values())
+
+
+def test_merge_partials_validation():
+    assert _merge(R=576) == -2 and _merge(dt=2) == -2   # R must be 512/256; fp8 is no output dtype
+    assert _merge(G=0) == -1 and _merge(H=0) == -1 and _merge(B=-1) == -1
+    assert _merge(o_parts=None) == -1 and _merge(lse_parts=None) == -1
+    assert _merge(o=None) == -1 and _merge(lse=None) == -1
+    assert _merge(o_parts=FAKE + 8) == -1               # not 16-byte aligned
+    assert _merge(o=FAKE + 4) == -1
+    assert _merge(lse=FAKE + 2) == -1
+    assert _merge(B=0) == 0                             # nothing launched
+
+
+def test_binding_rejects_host_tensors_and_bad_shapes():
+    """The binding refuses tensors the library cannot address (host memory)
+    and shapes that do not match, before any call into the library."""
+    import torch
+    import mla_paged_decode_concat_amd as M
+    q = torch.zeros((2, 4, 576), dtype=torch.bfloat16)
+    cache = torch.zeros((3, 16, 576), dtype=torch.bfloat16)
+    table = torch.zeros((2, 3), dtype=torch.int32)
+    lens = torch.ones(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        M.decode(q, cache, table, lens, 0.1, 1)
+    with pytest.raises(ValueError, match="B entries"):
+        M.decode(q, cache, table, torch.ones(3, dtype=torch.int32), 0.1, 1)
+    with pytest.raises(ValueError, match="R \\+ P"):
+        M.decode(q, torch.zeros((3, 16, 512), dtype=torch.bfloat16), table, lens, 0.1, 1)
+    kv_c = torch.zeros((5, 512), dtype=torch.bfloat16)
+    k_pe = torch.zeros((5, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        M.cache_write(kv_c, k_pe, cache, torch.zeros(5, dtype=torch.int64))
+    with pytest.raises(ValueError, match="one row per"):
+        M.cache_write(kv_c, k_pe, cache, torch.zeros(6, dtype=torch.int64))
+    with pytest.raises(ValueError, match="GPU tensors"):
+        M.merge_partials(torch.zeros((2, 2, 4, 512)), torch.zeros((2, 2, 4)))
+    with pytest.raises(ValueError, match="fp32 \\[G, B, H\\]"):
+        M.merge_partials(torch.zeros((2, 2, 4, 512)), torch.zeros((2, 2, 5)))
