@@ -221,3 +221,28 @@ def multi_token_q(bt: Batch, q_len: int, seed: Optional[int] = None) -> torch.Te
     g.manual_seed(2000 + spec.index if seed is None else seed)
     shape = (bt.B, q_len, spec.H, spec.D)
     return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch_dtype(spec.in_dtype))
+
+
+ROPE_THETA = 10000.0   # rope_theta of DeepSeek-V2/V3
+
+
+def rope_table(max_position: int, P: int = 64, theta: float = ROPE_THETA) -> torch.Tensor:
+    """A rotary table [max_position, P] float32: P/2 cosines then P/2 sines of
+    position * theta^(-2i/P), evaluated in float64 on the CPU.  It stands in
+    for the model's (YaRN-scaled) table, which is an input of the rotary
+    step; any table of angles exercises the same arithmetic."""
+    pos = torch.arange(max_position, dtype=torch.float64)[:, None]
+    inv = theta ** (-torch.arange(0, P, 2, dtype=torch.float64) / P)
+    ang = pos * inv[None, :]
+    return torch.cat([torch.cos(ang), torch.sin(ang)], dim=1).to(torch.float32)
+
+
+def token_positions(bt: Batch) -> torch.Tensor:
+    """Position of every row of kv_c/k_pe within its request (int64 [T]);
+    padded rows (slot -1) get position 0."""
+    pos = torch.zeros(bt.slot_mapping.numel(), dtype=torch.int64)
+    slots = bt.slot_mapping.cpu()
+    real = torch.nonzero(slots >= 0).flatten()
+    within = torch.cat([torch.arange(n, dtype=torch.int64) for n in bt.seq_lens_list]) if real.numel() else real
+    pos[real] = within
+    return pos.to(bt.slot_mapping.device)

@@ -189,6 +189,87 @@ def cache_write(cache: np.ndarray, kv_c: np.ndarray, k_pe: np.ndarray,
 
 
 # ---------------------------------------------------------------------------
+# Rotary position embedding on the rope part, fused into the write
+# [DIFF: MLA decode path, rotary_emb(input_positions, q_pe, k_pe) applied
+#  before the cache write; DeepSeek-V2 attention, get_rope(...,
+#  rope_type 'deepseek_yarn', is_neox_style=False)]
+# ---------------------------------------------------------------------------
+
+def rope_rotate_f32(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Rotary embedding in the non-NeoX form: element pairs (x[2i], x[2i+1])
+    of the last axis (length P) are rotated by angle i, whose cosine and sine
+    are cos[..., i] and sin[..., i] (P/2 each):
+        x'[2i]   = x[2i] cos_i - x[2i+1] sin_i
+        x'[2i+1] = x[2i+1] cos_i + x[2i] sin_i.
+    The pages fix neither the precision nor the table; here the table is an
+    input and the arithmetic is float32 with each product and each sum
+    rounded to float32 (no fused multiply-add), the precision in which the
+    stored value is then decided."""
+    x = np.asarray(x, dtype=np.float32)
+    c = np.asarray(cos, dtype=np.float32)
+    s = np.asarray(sin, dtype=np.float32)
+    a = x[..., 0::2]
+    b = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = (a * c) - (b * s)
+    out[..., 1::2] = (b * c) + (a * s)
+    return out
+
+
+def encode_f32(v: np.ndarray, dtype: str, scale: float | None = None) -> np.ndarray:
+    """float32 values -> stored representation: fp32 as is, bf16 by
+    round-to-nearest-even, fp8 as E4M3 of v / scale (fp32 divide)."""
+    v = np.asarray(v, dtype=np.float32)
+    if dtype == "f32":
+        return v.copy()
+    if dtype == "bf16":
+        return f32_to_bf16_bits_rne(v)
+    if dtype == "fp8":
+        return fp8_e4m3fn_encode(v / np.float32(scale))
+    raise ValueError(dtype)
+
+
+def rope_table_rows(cos_sin_cache: np.ndarray, positions: np.ndarray, P: int):
+    """cos and sin rows of a table laid out [max_position, P] as P/2 cosines
+    followed by P/2 sines (the rotary module's cache layout)."""
+    rows = np.asarray(cos_sin_cache, dtype=np.float32)[np.asarray(positions, dtype=np.int64)]
+    return rows[..., :P // 2], rows[..., P // 2:P]
+
+
+def cache_write_rope(cache: np.ndarray, kv_c: np.ndarray, k_pe: np.ndarray, positions: np.ndarray,
+                     cos_sin_cache: np.ndarray, slot_mapping: np.ndarray, in_dtype: str, cache_dtype: str,
+                     scale: float | None = None) -> np.ndarray:
+    """``cache_write`` with the rotary embedding of each token's position
+    applied to k_pe first: the kv_c columns are written as by ``cache_write``;
+    the k_pe columns hold encode(rope_rotate_f32(k_pe, cos, sin)).  Tokens
+    with a negative slot are skipped (their position is not read)."""
+    out = cache_write(cache, kv_c, k_pe, slot_mapping, in_dtype, cache_dtype, scale)
+    nb, bs, D = out.shape
+    R = kv_c.shape[1]
+    P = k_pe.shape[1]
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    tok = np.nonzero(slots >= 0)[0]
+    c, s = rope_table_rows(cos_sin_cache, np.asarray(positions)[tok], P)
+    rot = rope_rotate_f32(to_f32_exact(k_pe[tok, :P], in_dtype), c, s)
+    out[slots[tok] // bs, slots[tok] % bs, R:] = encode_f32(rot, cache_dtype, scale)
+    return out
+
+
+def rope_q(q: np.ndarray, positions: np.ndarray, cos_sin_cache: np.ndarray, q_dtype: str,
+           kv_lora_rank: int) -> np.ndarray:
+    """q [N, H, R + P] with the rope part q[..., R:] of token n rotated by
+    position positions[n] and stored back in q's dtype; the first R columns
+    are unchanged."""
+    out = np.array(q, copy=True)
+    R = kv_lora_rank
+    P = out.shape[-1] - R
+    c, s = rope_table_rows(cos_sin_cache, positions, P)
+    rot = rope_rotate_f32(to_f32_exact(out[..., R:], q_dtype), c[:, None, :], s[:, None, :])
+    out[..., R:] = encode_f32(rot, q_dtype)
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Decode
 # ---------------------------------------------------------------------------
 
