@@ -211,9 +211,14 @@ def main():
     if not args.main_only:
         # the rows beyond the single-token step, each timed on its own with events
         def timed_us(fn, n=10):
+            """GPU time per call: the stream is held by a spin kernel while
+            the n calls are queued behind the start event, so host-side
+            launch overhead does not show as idle time between them."""
             for _ in range(3):
                 fn()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            torch.cuda._sleep(5_000_000)
             a.record()
             for _ in range(n):
                 fn()
@@ -242,11 +247,25 @@ def main():
         merge_us = timed_us(lambda: M.merge_partials(o_parts, lse_parts, om, lm), n=20)
         merge_bytes = G8 * B * H * (R * 2 + 4) + B * H * (R * 2 + 4)
         del o_parts, lse_parts
+        # RoPE fused into the write: the whole context, and the step's 64
+        # tokens with the query's rope part rotated at the newest positions
+        tab = W.rope_table(8192, spec.P).to(dev)
+        pos = W.token_positions(bt)
+        rope_bulk_us = timed_us(lambda: M.cache_write(bt.kv_c, bt.k_pe, bt.cache, bt.slot_mapping, "auto",
+                                                      positions=pos, cos_sin_cache=tab), n=3)
+        step_pos = pos.index_select(0, idx)
+        qr = bt.q.clone()
+        rope_step_us = timed_us(lambda: (M.cache_write(step_kv_c, step_k_pe, bt.cache, step_slots, "auto",
+                                                       positions=step_pos, cos_sin_cache=tab),
+                                         M.rope_q(qr, step_pos, tab, R)), n=20)
+        del qr
         extras = {
             "decode_us_q_len1": round(dec1_us, 2),
             "decode_us_q_len2_noncausal": round(mtok_us, 2),
             "shard_merge_g8_us": round(merge_us, 2),
             "shard_merge_g8_gbps": round(merge_bytes / (merge_us * 1e-6) / 1e9, 1),
+            "cache_write_rope_bulk_gbps": round((bulk_bytes + N * 8) / (rope_bulk_us * 1e-6) / 1e9, 1),
+            "step_write_rope_plus_q_rope_us": round(rope_step_us, 2),
         }
 
     if args.copy_probe_mb:

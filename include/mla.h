@@ -141,6 +141,63 @@ int mla_cache_write(const void* kv_c, int64_t kv_c_row_stride,
                     const float* scale, void* stream);
 
 /*
+ * Cache write with the rotary position embedding of k_pe fused in: the same
+ * write as mla_cache_write, except that the k_pe columns of token t hold
+ * enc(rot(k_pe[t], positions[t])).  rot turns each interleaved pair
+ * (x[2i], x[2i+1]) by the angle whose cosine and sine are
+ *   cos_sin_cache[positions[t] * P + i]  and  cos_sin_cache[positions[t] * P + P/2 + i]:
+ *   (x[2i] cos - x[2i+1] sin,  x[2i+1] cos + x[2i] sin),
+ * in fp32 with each product and sum rounded to fp32 (no fused multiply-add);
+ * enc stores that fp32 value in the cache's type (bf16: round to nearest
+ * even; fp8: divide by *scale, then as mla_cache_write).  kv_c is written
+ * exactly as by mla_cache_write.  k_pe itself is not modified.
+ * [DIFF: MLA decode path, rotary_emb(input_positions, q_pe, k_pe) ahead of
+ *  the cache write; DeepSeek-V2 attention, get_rope with rope_type
+ *  'deepseek_yarn' and is_neox_style=False (interleaved pairs)]
+ *
+ *   positions      : int64 [num_tokens], device; the position of each token
+ *   cos_sin_cache  : fp32 [max_position, P], device, 4-byte aligned (16 for the
+ *                    vectorised path): P/2 cosines then P/2 sines per row --
+ *                    the caller's table (YaRN scaling, if any, is folded in)
+ *   max_position   : rows in cos_sin_cache, >= 1
+ *   other arguments: as mla_cache_write.
+ * Preconditions (device data): 0 <= positions[t] < max_position for tokens
+ * with a non-negative slot (a position outside is clamped to the nearest
+ * row rather than read out of bounds); positions of padded tokens are not read.
+ * Errors: as mla_cache_write; MLA_ERR_ARG also for max_position < 1 or a NULL
+ * positions / cos_sin_cache when num_tokens > 0.
+ */
+int mla_cache_write_rope(const void* kv_c, int64_t kv_c_row_stride,
+                         const void* k_pe, int64_t k_pe_row_stride, int in_dtype,
+                         const int64_t* slot_mapping, int64_t num_tokens,
+                         const int64_t* positions, const float* cos_sin_cache, int64_t max_position,
+                         void* cache, int cache_dtype,
+                         int64_t num_blocks, int block_size, int64_t block_stride,
+                         int kv_lora_rank, int rope_dim,
+                         const float* scale, void* stream);
+
+/*
+ * Rotary embedding of the query's rope part, in place: for every token n and
+ * head h, q[n][h][R : R + P) is rotated by positions[n] exactly as k_pe is
+ * in mla_cache_write_rope and stored back in q's dtype (bf16: round to
+ * nearest even).  The first R columns are not touched.
+ * [DIFF: MLA decode path, rotary_emb(input_positions, q_pe, k_pe)]
+ *
+ *   q                       : [num_tokens, H, R + P], device, element type q_dtype
+ *   q_stride_n, q_stride_h  : strides in elements (q_stride_h >= R + P,
+ *                             q_stride_n >= H * q_stride_h)
+ *   q_dtype                 : MLA_F32 or MLA_BF16
+ *   positions, cos_sin_cache, max_position : as mla_cache_write_rope
+ * A query block of q_len tokens per request ([B, q_len, H, R + P]) is
+ * num_tokens = B * q_len rows with a position per token.
+ * Errors: MLA_ERR_ARG, MLA_ERR_UNSUPPORTED (dtype, (R, P)), MLA_ERR_HIP.
+ * num_tokens == 0 launches nothing.
+ */
+int mla_rope_q(void* q, int64_t q_stride_n, int64_t q_stride_h, int q_dtype, int64_t num_tokens, int H,
+               int kv_lora_rank, int rope_dim, const int64_t* positions, const float* cos_sin_cache,
+               int64_t max_position, void* stream);
+
+/*
  * MLA decode over the paged latent cache: all H query heads attend to one
  * shared latent KV head (MQA form).
  * [ESSAY: Design motivation (single KV channel, head sizes 320/576, lse

@@ -14,4 +14,5 @@ from .binding import (  # noqa: F401
     load_library,
     merge_partials,
     num_kv_splits,
+    rope_q,
 )

@@ -20,7 +20,7 @@ MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace too small", -4: "HIP failure"}
 
 EXPORTS = ["mla_status_string", "mla_num_kv_splits", "mla_decode_workspace_bytes", "mla_cache_write",
-           "mla_decode", "mla_decode_ex", "mla_merge_partials"]
+           "mla_decode", "mla_decode_ex", "mla_merge_partials", "mla_cache_write_rope", "mla_rope_q"]
 
 
 class MLAError(RuntimeError):
@@ -67,6 +67,11 @@ def load_library():
     lib.mla_decode.argtypes = dec
     lib.mla_decode_ex.restype = i32
     lib.mla_decode_ex.argtypes = dec + [ctypes.POINTER(DecodeOpts)]
+    lib.mla_cache_write_rope.restype = i32
+    lib.mla_cache_write_rope.argtypes = [vp, i64, vp, i64, i32, vp, i64, vp, vp, i64, vp, i32, i64, i32, i64, i32,
+                                         i32, vp, vp]
+    lib.mla_rope_q.restype = i32
+    lib.mla_rope_q.argtypes = [vp, i64, i64, i32, i64, i32, i32, i32, vp, vp, i64, vp]
     lib.mla_merge_partials.restype = i32
     lib.mla_merge_partials.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
     _lib = lib
@@ -119,10 +124,13 @@ def decode_workspace_bytes(B: int, H: int, num_kv_splits: int, kv_lora_rank: int
 
 
 def cache_write(kv_c: torch.Tensor, k_pe: torch.Tensor, kv_cache: torch.Tensor, slot_mapping: torch.Tensor,
-                kv_cache_dtype: str = "auto", scale: Optional[torch.Tensor] = None) -> None:
+                kv_cache_dtype: str = "auto", scale: Optional[torch.Tensor] = None,
+                positions: Optional[torch.Tensor] = None, cos_sin_cache: Optional[torch.Tensor] = None) -> None:
     """Scatter kv_c [T', R] and k_pe [T', P] into kv_cache [num_blocks, block_size, R+P]
     at slot_mapping [T] (T <= T'; slot -1 = skip).  kv_cache_dtype "auto" stores
-    the input dtype; "fp8"/"fp8_e4m3" encodes with the device fp32 scalar ``scale``."""
+    the input dtype; "fp8"/"fp8_e4m3" encodes with the device fp32 scalar ``scale``.
+    With ``positions`` (int64 [T]) and ``cos_sin_cache`` (fp32 [max_position, P]:
+    cosines then sines) k_pe is rotated (interleaved pairs) before it is stored."""
     in_dt = _dtype_code(kv_c)
     cache_dt = _dtype_code(kv_cache)
     if kv_cache_dtype.startswith("fp8") != (cache_dt == MLA_FP8_E4M3):
@@ -139,14 +147,58 @@ def cache_write(kv_c: torch.Tensor, k_pe: torch.Tensor, kv_cache: torch.Tensor, 
         raise ValueError("kv_cache must be [num_blocks, block_size, R + P]")
     if scale is not None and scale.numel() < 1:
         raise ValueError("scale must hold one fp32 value")
-    _same_gpu(kv_c, k_pe, kv_cache, slot_mapping, scale)
-    st = load_library().mla_cache_write(
+    _same_gpu(kv_c, k_pe, kv_cache, slot_mapping, scale, positions, cos_sin_cache)
+    if (positions is None) != (cos_sin_cache is None):
+        raise ValueError("positions and cos_sin_cache go together")
+    lib = load_library()
+    if positions is None:
+        st = lib.mla_cache_write(
+            kv_c.data_ptr(), kv_c.stride(0), k_pe.data_ptr(), k_pe.stride(0), in_dt,
+            slot_mapping.data_ptr(), slot_mapping.numel(),
+            kv_cache.data_ptr(), cache_dt, kv_cache.shape[0], kv_cache.shape[1], kv_cache.stride(0),
+            kv_c.shape[1], k_pe.shape[1],
+            scale.data_ptr() if scale is not None else None, _stream(kv_c.device))
+        _check(st, "mla_cache_write")
+        return
+    _check_rope_args(positions, cos_sin_cache, slot_mapping.numel(), k_pe.shape[1])
+    st = lib.mla_cache_write_rope(
         kv_c.data_ptr(), kv_c.stride(0), k_pe.data_ptr(), k_pe.stride(0), in_dt,
-        slot_mapping.data_ptr(), slot_mapping.numel(),
+        slot_mapping.data_ptr(), slot_mapping.numel(), positions.data_ptr(), cos_sin_cache.data_ptr(),
+        cos_sin_cache.shape[0],
         kv_cache.data_ptr(), cache_dt, kv_cache.shape[0], kv_cache.shape[1], kv_cache.stride(0),
         kv_c.shape[1], k_pe.shape[1],
         scale.data_ptr() if scale is not None else None, _stream(kv_c.device))
-    _check(st, "mla_cache_write")
+    _check(st, "mla_cache_write_rope")
+
+
+def _check_rope_args(positions: torch.Tensor, cos_sin_cache: torch.Tensor, n: int, P: int) -> None:
+    if positions.dtype != torch.int64 or not positions.is_contiguous() or positions.numel() < n:
+        raise ValueError("positions must be contiguous int64 with one entry per token")
+    if cos_sin_cache.dtype != torch.float32 or not cos_sin_cache.is_contiguous() or cos_sin_cache.dim() != 2 \
+            or cos_sin_cache.shape[1] != P:
+        raise ValueError("cos_sin_cache must be contiguous fp32 [max_position, rope_dim]")
+
+
+def rope_q(q: torch.Tensor, positions: torch.Tensor, cos_sin_cache: torch.Tensor, kv_lora_rank: int = 512) -> torch.Tensor:
+    """Rotate the rope part q[..., R:] of q [N, H, R+P] (or [B, q_len, H, R+P],
+    one position per token) in place; returns q."""
+    if q.dim() == 4:
+        if q.stride(0) != q.shape[1] * q.stride(1):
+            raise ValueError("a [B, q_len, H, D] query needs batch stride q_len * token stride")
+        flat = torch.as_strided(q, (q.shape[0] * q.shape[1], q.shape[2], q.shape[3]),
+                                (q.stride(1), q.stride(2), q.stride(3)))
+        rope_q(flat, positions, cos_sin_cache, kv_lora_rank)
+        return q
+    N, H, D = q.shape
+    if q.stride(-1) != 1:
+        raise ValueError("rows must be contiguous")
+    _check_rope_args(positions, cos_sin_cache, N, D - kv_lora_rank)
+    _same_gpu(q, positions, cos_sin_cache)
+    st = load_library().mla_rope_q(q.data_ptr(), q.stride(0), q.stride(1), _dtype_code(q), N, H, kv_lora_rank,
+                                   D - kv_lora_rank, positions.data_ptr(), cos_sin_cache.data_ptr(),
+                                   cos_sin_cache.shape[0], _stream(q.device))
+    _check(st, "mla_rope_q")
+    return q
 
 
 def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,

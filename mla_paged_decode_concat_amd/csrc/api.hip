@@ -61,13 +61,15 @@ size_t mla_decode_workspace_bytes(int B, int H, int num_kv_splits, int kv_lora_r
   return (size_t)B * (size_t)H * (size_t)num_kv_splits * ((size_t)kv_lora_rank + 1) * sizeof(float);
 }
 
-int mla_cache_write(const void* kv_c, int64_t kv_c_row_stride,
-                    const void* k_pe, int64_t k_pe_row_stride, int in_dtype,
-                    const int64_t* slot_mapping, int64_t num_tokens,
-                    void* cache, int cache_dtype,
-                    int64_t num_blocks, int block_size, int64_t block_stride,
-                    int kv_lora_rank, int rope_dim,
-                    const float* scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int cache_write_impl(const void* kv_c, int64_t kv_c_row_stride, const void* k_pe, int64_t k_pe_row_stride,
+                     int in_dtype, const int64_t* slot_mapping, int64_t num_tokens, void* cache, int cache_dtype,
+                     int64_t num_blocks, int block_size, int64_t block_stride, int kv_lora_rank, int rope_dim,
+                     const float* scale, const int64_t* positions, const float* rope, int64_t max_position,
+                     void* stream) {
   if (in_dtype != MLA_F32 && in_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
   if (cache_dtype != in_dtype && cache_dtype != MLA_FP8_E4M3) return MLA_ERR_UNSUPPORTED;
   if (!shape_supported(kv_lora_rank, rope_dim)) return MLA_ERR_UNSUPPORTED;
@@ -93,6 +95,9 @@ int mla_cache_write(const void* kv_c, int64_t kv_c_row_stride,
   p.P = rope_dim;
   p.scale = scale;
   p.tokens_per_wave = write_tokens_per_wave(num_tokens);
+  p.positions = positions;
+  p.rope = rope;
+  p.max_position = max_position;
 
   const int ib = elem_bytes(in_dtype), cb = elem_bytes(cache_dtype);
   const int out_vec = 16 / ib * cb;   // bytes written per 16-byte input vector
@@ -100,9 +105,69 @@ int mla_cache_write(const void* kv_c, int64_t kv_c_row_stride,
                    (kv_c_row_stride * ib) % 16 == 0 && (k_pe_row_stride * ib) % 16 == 0 &&
                    (reinterpret_cast<uintptr_t>(cache) % out_vec) == 0 &&
                    (block_stride * cb) % out_vec == 0 && ((int64_t)D * cb) % out_vec == 0 &&
-                   ((int64_t)kv_lora_rank * cb) % out_vec == 0;
+                   ((int64_t)kv_lora_rank * cb) % out_vec == 0 && (rope == nullptr || aligned16(rope));
   (void)hipGetLastError();
   hipError_t e = launch_cache_write(in_dtype, cache_dtype, p, vec, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_cache_write(const void* kv_c, int64_t kv_c_row_stride,
+                    const void* k_pe, int64_t k_pe_row_stride, int in_dtype,
+                    const int64_t* slot_mapping, int64_t num_tokens,
+                    void* cache, int cache_dtype,
+                    int64_t num_blocks, int block_size, int64_t block_stride,
+                    int kv_lora_rank, int rope_dim,
+                    const float* scale, void* stream) {
+  return cache_write_impl(kv_c, kv_c_row_stride, k_pe, k_pe_row_stride, in_dtype, slot_mapping, num_tokens, cache,
+                          cache_dtype, num_blocks, block_size, block_stride, kv_lora_rank, rope_dim, scale, nullptr,
+                          nullptr, 0, stream);
+}
+
+int mla_cache_write_rope(const void* kv_c, int64_t kv_c_row_stride,
+                         const void* k_pe, int64_t k_pe_row_stride, int in_dtype,
+                         const int64_t* slot_mapping, int64_t num_tokens,
+                         const int64_t* positions, const float* cos_sin_cache, int64_t max_position,
+                         void* cache, int cache_dtype,
+                         int64_t num_blocks, int block_size, int64_t block_stride,
+                         int kv_lora_rank, int rope_dim,
+                         const float* scale, void* stream) {
+  if (max_position < 1) return MLA_ERR_ARG;
+  if (num_tokens > 0 && (!positions || !cos_sin_cache)) return MLA_ERR_ARG;
+  if (cos_sin_cache && reinterpret_cast<uintptr_t>(cos_sin_cache) % 4 != 0) return MLA_ERR_ARG;
+  return cache_write_impl(kv_c, kv_c_row_stride, k_pe, k_pe_row_stride, in_dtype, slot_mapping, num_tokens, cache,
+                          cache_dtype, num_blocks, block_size, block_stride, kv_lora_rank, rope_dim, scale, positions,
+                          cos_sin_cache, max_position, stream);
+}
+
+int mla_rope_q(void* q, int64_t q_stride_n, int64_t q_stride_h, int q_dtype, int64_t num_tokens, int H,
+               int kv_lora_rank, int rope_dim, const int64_t* positions, const float* cos_sin_cache,
+               int64_t max_position, void* stream) {
+  if (q_dtype != MLA_F32 && q_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (!shape_supported(kv_lora_rank, rope_dim)) return MLA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || H < 1 || max_position < 1) return MLA_ERR_ARG;
+  if (q_stride_h < kv_lora_rank + rope_dim || q_stride_n < (int64_t)H * q_stride_h) return MLA_ERR_ARG;
+  if (num_tokens == 0) return MLA_OK;
+  if (!q || !positions || !cos_sin_cache) return MLA_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(q) % elem_bytes(q_dtype) != 0 ||
+      reinterpret_cast<uintptr_t>(cos_sin_cache) % 4 != 0)
+    return MLA_ERR_ARG;
+  RopeQParams p;
+  p.q = q;
+  p.q_sn = q_stride_n;
+  p.q_sh = q_stride_h;
+  p.N = num_tokens;
+  p.H = H;
+  p.R = kv_lora_rank;
+  p.P = rope_dim;
+  p.positions = positions;
+  p.rope = cos_sin_cache;
+  p.max_position = max_position;
+  (void)hipGetLastError();
+  const hipError_t e = launch_rope_q(q_dtype, p, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

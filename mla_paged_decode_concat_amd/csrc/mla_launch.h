@@ -20,11 +20,27 @@ struct WriteParams {
   int R, P;
   const float* scale;
   int tokens_per_wave;                  // write_tokens_per_wave(num_tokens)
+  // rotary embedding of k_pe (rope == nullptr: none): per-token positions
+  // and a [max_position, P] fp32 table of P/2 cosines then P/2 sines
+  const int64_t* positions;
+  const float* rope;
+  long long max_position;
+};
+
+struct RopeQParams {
+  void* q;
+  long long q_sn, q_sh;                 // elements
+  long long N;
+  int H, R, P;
+  const int64_t* positions;
+  const float* rope;
+  long long max_position;
 };
 
 int write_tokens_per_wave(long long num_tokens);
 
 hipError_t launch_cache_write(int in_dtype, int cache_dtype, const WriteParams& p, bool vec, hipStream_t stream);
+hipError_t launch_rope_q(int q_dtype, const RopeQParams& p, hipStream_t stream);
 
 hipError_t launch_stage1_valu(int q_dtype, int cache_dtype, int R, const DecodeParams& p, hipStream_t stream);
 hipError_t launch_stage1_mfma(int cache_dtype, int R, const DecodeParams& p, hipStream_t stream);

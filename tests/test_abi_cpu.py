@@ -168,3 +168,35 @@ def test_binding_rejects_host_tensors_and_bad_shapes():
         M.merge_partials(torch.zeros((2, 2, 4, 512)), torch.zeros((2, 2, 4)))
     with pytest.raises(ValueError, match="fp32 \\[G, B, H\\]"):
         M.merge_partials(torch.zeros((2, 2, 4, 512)), torch.zeros((2, 2, 5)))
+
+
+def _wrope(**kw):
+    a = dict(kv_c=FAKE, kvs=512, k_pe=FAKE, kps=64, in_dt=1, slots=FAKE, T=10, pos=FAKE, tab=FAKE, maxpos=100,
+             cache=FAKE, cache_dt=1, nb=4, bs=16, bstride=16 * 576, R=512, P=64, scale=None, stream=None)
+    a.update(kw)
+    return binding.load_library().mla_cache_write_rope(*a.values())
+
+
+def test_cache_write_rope_validation():
+    assert _wrope(maxpos=0) == -1
+    assert _wrope(pos=None) == -1 and _wrope(tab=None) == -1
+    assert _wrope(tab=FAKE + 2) == -1                 # table not 4-byte aligned
+    assert _wrope(in_dt=2) == -2 and _wrope(R=128) == -2
+    assert _wrope(cache_dt=2) == -1                   # fp8 cache without a scale
+    assert _wrope(T=0, pos=None, tab=None) == 0       # nothing to do
+
+
+def _ropeq(**kw):
+    a = dict(q=FAKE, sn=128 * 576, sh=576, dt=1, N=4, H=128, R=512, P=64, pos=FAKE, tab=FAKE, maxpos=100,
+             stream=None)
+    a.update(kw)
+    return binding.load_library().mla_rope_q(*a.values())
+
+
+def test_rope_q_validation():
+    assert _ropeq(dt=2) == -2 and _ropeq(P=32) == -2
+    assert _ropeq(H=0) == -1 and _ropeq(N=-1) == -1 and _ropeq(maxpos=0) == -1
+    assert _ropeq(sh=575) == -1 and _ropeq(sn=127 * 576) == -1
+    assert _ropeq(q=None) == -1 and _ropeq(pos=None) == -1 and _ropeq(tab=None) == -1
+    assert _ropeq(q=FAKE + 1) == -1 and _ropeq(tab=FAKE + 2) == -1
+    assert _ropeq(N=0) == 0
