@@ -270,6 +270,61 @@ def rope_q(q: np.ndarray, positions: np.ndarray, cos_sin_cache: np.ndarray, q_dt
 
 
 # ---------------------------------------------------------------------------
+# Absorbed projections around the decode  [DIFF: MLACommonImpl docstring,
+#  decode steps 3, 7 and 11 (weight absorption by associativity);
+#  _q_proj_and_k_up_proj, _v_up_proj_and_o_proj and
+#  process_weights_after_loading]
+# ---------------------------------------------------------------------------
+
+def linear(A: np.ndarray, W: np.ndarray, in_dtype: str = "bf16") -> np.ndarray:
+    """C = A W^T in float64: A [M, K] and W [N, K] (a linear layer's weight,
+    one row per output feature) in their stored representation."""
+    return to_f64(A, in_dtype) @ to_f64(W, in_dtype).T
+
+
+def absorb_q_weight(W_Q: np.ndarray, W_UK: np.ndarray) -> np.ndarray:
+    """The q-side absorbed weight in linear-layer layout [N * Lkv, Lq]:
+    row (n, l) is sum_p W_Q[:, n, p] W_UK[l, n, p], so that
+    q_c W_Q_UK^T, viewed [B, N, Lkv], is q_nope after the k up-projection.
+    W_Q [Lq, N, P] (the nope part of the q projection, input-major as the
+    pages lay it out) and W_UK [Lkv, N, P], float64."""
+    Lq, N, P = W_Q.shape
+    Lkv = W_UK.shape[0]
+    out = np.empty((N, Lkv, Lq))
+    for n in range(N):
+        out[n] = W_UK[:, n, :] @ W_Q[:, n, :].T
+    return out.reshape(N * Lkv, Lq)
+
+
+def absorb_o_weight(W_UV: np.ndarray, W_O: np.ndarray) -> np.ndarray:
+    """The output-side absorbed weight in linear-layer layout [Hid, N * Lkv]:
+    entry (h, (n, l)) is sum_v W_UV[l, n, v] W_O[h, n, v], so that the decode
+    output [B, N, Lkv] flattened times its transpose is the o projection of
+    the v up-projection.  W_UV [Lkv, N, V], W_O [Hid, N, V], float64."""
+    Lkv, N, V = W_UV.shape
+    Hid = W_O.shape[0]
+    out = np.empty((Hid, N, Lkv))
+    for n in range(N):
+        out[:, n, :] = W_O[:, n, :] @ W_UV[:, n, :].T
+    return out.reshape(Hid, N * Lkv)
+
+
+def q_nope_unabsorbed(q_c: np.ndarray, W_Q: np.ndarray, W_UK: np.ndarray) -> np.ndarray:
+    """q_nope [B, N, Lkv] the long way: x = q_c W_Q per head [B, N, P], then
+    the k up-projection per head, q_nope[b, n, l] = sum_p x[b, n, p] W_UK[l, n, p]."""
+    Lq, N, P = W_Q.shape
+    x = (q_c @ W_Q.reshape(Lq, N * P)).reshape(-1, N, P)
+    return np.einsum("bnp,lnp->bnl", x, W_UK)
+
+
+def out_unabsorbed(o: np.ndarray, W_UV: np.ndarray, W_O: np.ndarray) -> np.ndarray:
+    """Output projection the long way: v[b, n, :] = o[b, n, :] W_UV[:, n, :]
+    per head, then out[b, h] = sum_{n, v} v[b, n, v] W_O[h, n, v]."""
+    v = np.einsum("bnl,lnv->bnv", o, W_UV)
+    return np.einsum("bnv,hnv->bh", v, W_O)
+
+
+# ---------------------------------------------------------------------------
 # Decode
 # ---------------------------------------------------------------------------
 
