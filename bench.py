@@ -259,6 +259,18 @@ def main():
                                                        positions=step_pos, cos_sin_cache=tab),
                                          M.rope_q(qr, step_pos, tab, R)), n=20)
         del qr
+        # absorbed projections at the DeepSeek-V3 per-GPU shape, batch 64:
+        # q_c [64, 1536] x W_Q_UK^T -> [64, 128*512]; o [64, 128*512] x W_UV_O^T -> [64, 7168]
+        gq = torch.Generator(device=dev).manual_seed(7)
+        lin = {}
+        for name, (Nf, Kf) in {"q_absorbed": (H * R, 1536), "o_absorbed": (7168, H * R)}.items():
+            Aq = torch.randn((B, Kf), generator=gq, device=dev).to(torch.bfloat16)
+            Wq = torch.randn((Nf, Kf), generator=gq, device=dev).to(torch.bfloat16)
+            Cq = torch.empty((B, Nf), dtype=torch.bfloat16, device=dev)
+            wsq = torch.empty(max(1, M.linear_workspace_bytes(B, Nf, Kf) // 4), dtype=torch.float32, device=dev)
+            us = timed_us(lambda: M.linear(Aq, Wq, out=Cq, workspace=wsq), n=10)
+            lin[name] = (us, (Nf * Kf + B * Kf + B * Nf) * 2)
+            del Aq, Wq, Cq, wsq
         extras = {
             "decode_us_q_len1": round(dec1_us, 2),
             "decode_us_q_len2_noncausal": round(mtok_us, 2),
@@ -266,6 +278,10 @@ def main():
             "shard_merge_g8_gbps": round(merge_bytes / (merge_us * 1e-6) / 1e9, 1),
             "cache_write_rope_bulk_gbps": round((bulk_bytes + N * 8) / (rope_bulk_us * 1e-6) / 1e9, 1),
             "step_write_rope_plus_q_rope_us": round(rope_step_us, 2),
+            "linear_q_absorbed_us": round(lin["q_absorbed"][0], 2),
+            "linear_q_absorbed_gbps": round(lin["q_absorbed"][1] / (lin["q_absorbed"][0] * 1e-6) / 1e9, 1),
+            "linear_o_absorbed_us": round(lin["o_absorbed"][0], 2),
+            "linear_o_absorbed_gbps": round(lin["o_absorbed"][1] / (lin["o_absorbed"][0] * 1e-6) / 1e9, 1),
         }
 
     if args.copy_probe_mb:

@@ -198,6 +198,36 @@ int mla_rope_q(void* q, int64_t q_stride_n, int64_t q_stride_h, int q_dtype, int
                int64_t max_position, void* stream);
 
 /*
+ * Linear layer for the absorbed projections around the decode:
+ *   C[m][n] = sum_k A[m][k] * W[n][k]
+ * with bf16 A and W, fp32 accumulation, C in fp32 or bf16 (round to nearest
+ * even).  With weight absorption the q side is q_nope = q_c W_Q_UK and the
+ * output side is out = o W_UV_O, both plain products of a decode batch with
+ * a precomputed weight [DIFF: MLACommonImpl docstring, decode steps 3, 7 and
+ * 11; _q_proj_and_k_up_proj and _v_up_proj_and_o_proj;
+ * process_weights_after_loading builds W_Q_UK and W_UV_O].
+ *
+ *   A, lda      : bf16 [M, K] rows (lda >= K, a multiple of 8), 16-byte aligned
+ *   W, ldw      : bf16 [N, K] rows -- a linear layer's weight, one row per
+ *                 output feature (ldw >= K, a multiple of 8), 16-byte aligned
+ *   M, N, K     : M >= 0 (any; processed 64 rows per launch),
+ *                 N a multiple of 16, K a multiple of 64
+ *   C, ldc      : [M, N] rows of c_dtype (ldc >= N, a multiple of 4);
+ *                 16-byte aligned for fp32, 8-byte for bf16
+ *   c_dtype     : MLA_F32 or MLA_BF16
+ *   workspace   : fp32 scratch of >= mla_linear_workspace_bytes(M, N, K)
+ *                 bytes, 16-byte aligned (may be NULL when that is 0): when the
+ *                 output features alone cannot fill the GPU, K is split over
+ *                 workgroups and the partials are summed in a fixed order
+ * The result does not depend on how the rows are batched.  Errors:
+ * MLA_ERR_UNSUPPORTED (c_dtype, N, K), MLA_ERR_ARG (strides, alignment, NULL),
+ * MLA_ERR_WORKSPACE, MLA_ERR_HIP.  M == 0 launches nothing.
+ */
+size_t mla_linear_workspace_bytes(int M, int N, int K);
+int mla_linear_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, int M, int N, int K,
+                    void* C, int64_t ldc, int c_dtype, float* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * MLA decode over the paged latent cache: all H query heads attend to one
  * shared latent KV head (MQA form).
  * [ESSAY: Design motivation (single KV channel, head sizes 320/576, lse

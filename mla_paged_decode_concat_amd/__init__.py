@@ -11,6 +11,8 @@ from .binding import (  # noqa: F401
     decode,
     decode_workspace_bytes,
     library_path,
+    linear,
+    linear_workspace_bytes,
     load_library,
     merge_partials,
     num_kv_splits,

@@ -20,7 +20,8 @@ MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace too small", -4: "HIP failure"}
 
 EXPORTS = ["mla_status_string", "mla_num_kv_splits", "mla_decode_workspace_bytes", "mla_cache_write",
-           "mla_decode", "mla_decode_ex", "mla_merge_partials", "mla_cache_write_rope", "mla_rope_q"]
+           "mla_decode", "mla_decode_ex", "mla_merge_partials", "mla_cache_write_rope", "mla_rope_q",
+           "mla_linear_bf16", "mla_linear_workspace_bytes"]
 
 
 class MLAError(RuntimeError):
@@ -72,6 +73,10 @@ def load_library():
                                          i32, vp, vp]
     lib.mla_rope_q.restype = i32
     lib.mla_rope_q.argtypes = [vp, i64, i64, i32, i64, i32, i32, i32, vp, vp, i64, vp]
+    lib.mla_linear_workspace_bytes.restype = sz
+    lib.mla_linear_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.mla_linear_bf16.restype = i32
+    lib.mla_linear_bf16.argtypes = [vp, i64, vp, i64, i32, i32, i32, vp, i64, i32, vp, sz, vp]
     lib.mla_merge_partials.restype = i32
     lib.mla_merge_partials.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
     _lib = lib
@@ -292,3 +297,33 @@ def merge_partials(o_parts: torch.Tensor, lse_parts: torch.Tensor, o: Optional[t
                                            _stream(o_parts.device))
     _check(st, "mla_merge_partials")
     return o, lse
+
+
+def linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(load_library().mla_linear_workspace_bytes(M, N, K))
+
+
+def linear(A: torch.Tensor, W: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = A W^T for bf16 A [M, K] and a bf16 weight W [N, K] (linear-layer
+    layout), fp32 accumulation, C [M, N] in ``out_dtype`` (fp32 or bf16)."""
+    M, K = A.shape
+    N, K2 = W.shape
+    if K2 != K or A.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+        raise ValueError("A [M, K] and W [N, K] must both be bf16")
+    if A.stride(-1) != 1 or W.stride(-1) != 1:
+        raise ValueError("rows must be contiguous")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    if tuple(out.shape) != (M, N) or out.stride(-1) != 1:
+        raise ValueError("out must be [M, N] with contiguous rows")
+    lib = load_library()
+    need = lib.mla_linear_workspace_bytes(M, N, K)
+    if need and workspace is None:
+        workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=A.device)
+    _same_gpu(A, W, out, workspace)
+    st = lib.mla_linear_bf16(A.data_ptr(), A.stride(0), W.data_ptr(), W.stride(0), M, N, K, out.data_ptr(),
+                             out.stride(0), _dtype_code(out), workspace.data_ptr() if workspace is not None else None,
+                             workspace.numel() * 4 if workspace is not None else 0, _stream(A.device))
+    _check(st, "mla_linear_bf16")
+    return out

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_amd.so")
 
-SOURCES = ["api.hip", "cache_write.hip", "decode_valu.hip", "decode_mfma.hip"]
+SOURCES = ["api.hip", "cache_write.hip", "decode_valu.hip", "decode_mfma.hip", "linear.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -275,6 +275,52 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
   return MLA_OK;
 }
 
+size_t mla_linear_workspace_bytes(int M, int N, int K) {
+  if (M < 1 || N < 16 || N % 16 != 0 || K < 64 || K % 64 != 0) return 0;
+  const int rows = M < 64 ? M : 64;
+  const int s = linear_splits(rows, N, K, device_cu_count());
+  return s > 1 ? (size_t)s * rows * N * sizeof(float) : 0;
+}
+
+int mla_linear_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, int M, int N, int K,
+                    void* C, int64_t ldc, int c_dtype, float* workspace, size_t workspace_bytes, void* stream) {
+  if (c_dtype != MLA_F32 && c_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (N < 16 || N % 16 != 0 || K < 64 || K % 64 != 0) return MLA_ERR_UNSUPPORTED;
+  if (M < 0 || lda < K || ldw < K || ldc < N) return MLA_ERR_ARG;
+  if (M == 0) return MLA_OK;
+  if (!A || !W || !C) return MLA_ERR_ARG;
+  if (!aligned16(A) || !aligned16(W) || lda % 8 != 0 || ldw % 8 != 0 || ldc % 4 != 0) return MLA_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(C) % (c_dtype == MLA_F32 ? 16 : 8) != 0) return MLA_ERR_ARG;
+  const int rows = M < 64 ? M : 64;
+  const int splits = linear_splits(rows, N, K, device_cu_count());
+  if (splits > 1) {
+    if (!workspace || !aligned16(workspace)) return MLA_ERR_ARG;
+    if (workspace_bytes < (size_t)splits * rows * N * sizeof(float)) return MLA_ERR_WORKSPACE;
+  }
+  LinearParams p;
+  p.W = W;
+  p.ldw = ldw;
+  p.lda = lda;
+  p.ldc = ldc;
+  p.N = N;
+  p.K = K;
+  p.ws = workspace;
+  const int ksteps = K / 64;
+  p.k_per_split = ((ksteps + splits - 1) / splits) * 64;
+  p.splits = (K + p.k_per_split - 1) / p.k_per_split;
+  (void)hipGetLastError();
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int cb = c_dtype == MLA_F32 ? 4 : 2;
+  // 64 batch rows per launch; launches on one stream reuse the workspace in order
+  for (int m0 = 0; m0 < M; m0 += 64) {
+    p.M = M - m0 < 64 ? M - m0 : 64;
+    p.A = static_cast<const uint16_t*>(A) + (int64_t)m0 * lda;
+    p.C = static_cast<char*>(C) + (int64_t)m0 * ldc * cb;
+    if (launch_linear(c_dtype, p, st) != hipSuccess) return MLA_ERR_HIP;
+  }
+  return MLA_OK;
+}
+
 int mla_merge_partials(const void* o_parts, const float* lse_parts, int G, int B, int H, int R, int dtype,
                        void* o, float* lse, void* stream) {
   if (R != 512 && R != 256) return MLA_ERR_UNSUPPORTED;

@@ -42,6 +42,19 @@ int write_tokens_per_wave(long long num_tokens);
 hipError_t launch_cache_write(int in_dtype, int cache_dtype, const WriteParams& p, bool vec, hipStream_t stream);
 hipError_t launch_rope_q(int q_dtype, const RopeQParams& p, hipStream_t stream);
 
+struct LinearParams {
+  const void* A;                        // bf16 [M, K], row stride lda
+  const void* W;                        // bf16 [N, K], row stride ldw
+  void* C;                              // [M, N], row stride ldc
+  float* ws;                            // split-K partials [splits, M, N] (splits > 1)
+  long long lda, ldw, ldc;
+  int M, N, K;                          // M <= 64 per launch
+  int splits, k_per_split;              // k_per_split a multiple of 64
+};
+
+int linear_splits(int M, int N, int K, int cus);
+hipError_t launch_linear(int c_dtype, const LinearParams& p, hipStream_t stream);
+
 hipError_t launch_stage1_valu(int q_dtype, int cache_dtype, int R, const DecodeParams& p, hipStream_t stream);
 hipError_t launch_stage1_mfma(int cache_dtype, int R, const DecodeParams& p, hipStream_t stream);
 hipError_t launch_stage2(int q_dtype, int R, const DecodeParams& p, hipStream_t stream);

@@ -246,3 +246,24 @@ def token_positions(bt: Batch) -> torch.Tensor:
     within = torch.cat([torch.arange(n, dtype=torch.int64) for n in bt.seq_lens_list]) if real.numel() else real
     pos[real] = within
     return pos.to(bt.slot_mapping.device)
+
+
+# DeepSeek-V3 projection sizes around the decode: q_lora_rank, heads,
+# qk_nope_head_dim, kv_lora_rank, v_head_dim, hidden size
+V3_PROJ = dict(Lq=1536, N=128, P=128, Lkv=512, V=128, Hid=7168)
+
+
+def projection_inputs(B: int, Lq: int, N: int, P: int, Lkv: int, V: int, Hid: int, seed: int = 3000,
+                      device="cpu"):
+    """Random bf16 projection weights in the pages' layouts and a q_c batch:
+    W_Q [Lq, N, P], W_UK [Lkv, N, P], W_UV [Lkv, N, V], W_O [Hid, N, V] with
+    N(0, 1/fan_in) entries, and q_c [B, Lq] ~ N(0, 1).  Drawn in float32 on a
+    CPU generator and cast to bf16 (round to nearest even)."""
+    g = torch.Generator().manual_seed(seed)
+    bf = torch.bfloat16
+    q_c = torch.randn((B, Lq), generator=g).to(bf)
+    W_Q = (torch.randn((Lq, N, P), generator=g) / math.sqrt(Lq)).to(bf)
+    W_UK = (torch.randn((Lkv, N, P), generator=g) / math.sqrt(P)).to(bf)
+    W_UV = (torch.randn((Lkv, N, V), generator=g) / math.sqrt(Lkv)).to(bf)
+    W_O = (torch.randn((Hid, N, V), generator=g) / math.sqrt(N * V)).to(bf)
+    return {k: v.to(device) for k, v in dict(q_c=q_c, W_Q=W_Q, W_UK=W_UK, W_UV=W_UV, W_O=W_O).items()}

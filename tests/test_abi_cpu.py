@@ -200,3 +200,24 @@ def test_rope_q_validation():
     assert _ropeq(q=None) == -1 and _ropeq(pos=None) == -1 and _ropeq(tab=None) == -1
     assert _ropeq(q=FAKE + 1) == -1 and _ropeq(tab=FAKE + 2) == -1
     assert _ropeq(N=0) == 0
+
+
+def _lin(**kw):
+    a = dict(A=FAKE, lda=1536, W=FAKE, ldw=1536, M=8, N=256, K=1536, C=FAKE, ldc=256, dt=1, ws=None, wsb=0,
+             stream=None)
+    a.update(kw)
+    return binding.load_library().mla_linear_bf16(*a.values())
+
+
+def test_linear_validation():
+    assert _lin(dt=2) == -2
+    assert _lin(N=24) == -2 and _lin(N=0) == -2 and _lin(K=96) == -2 and _lin(K=0) == -2
+    assert _lin(M=-1) == -1 and _lin(lda=1535) == -1 and _lin(ldw=1000) == -1 and _lin(ldc=255) == -1
+    assert _lin(A=None) == -1 and _lin(W=None) == -1 and _lin(C=None) == -1
+    assert _lin(A=FAKE + 8) == -1 and _lin(W=FAKE + 2) == -1 and _lin(lda=1544 + 4) == -1
+    assert _lin(C=FAKE + 4) == -1                    # bf16 output needs 8-byte alignment
+    assert _lin(C=FAKE + 8, dt=0) == -1              # fp32 output needs 16-byte alignment
+    assert _lin(M=0) == 0
+    lib = binding.load_library()
+    assert lib.mla_linear_workspace_bytes(8, 24, 1536) == 0          # unsupported N
+    assert lib.mla_linear_workspace_bytes(0, 256, 1536) == 0
