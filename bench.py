@@ -65,16 +65,18 @@ class HipEvent:
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_v3_b64_h128_n8192_hbm_traffic.txt")
 
 
+# the sources that define the stage-1 kernel and its launch (plan, grid)
+STAGE1_SOURCES = ["api.hip", "decode_mfma.hip", "mla_device.h", "mla_launch.h"]
+
+
 def kernel_sources_sha256() -> str:
-    """sha256 over the HIP sources of the library (file names and bytes)."""
-    import glob
+    """sha256 over the stage-1 kernel's sources (file names and bytes)."""
     import hashlib
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "mla_paged_decode_concat_amd", "csrc", "*"))):
-        if p.endswith((".hip", ".h")):
-            h.update(os.path.basename(p).encode())
-            with open(p, "rb") as f:
-                h.update(f.read())
+    for name in STAGE1_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(ROOT, "mla_paged_decode_concat_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
