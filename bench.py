@@ -361,18 +361,18 @@ def pct(sorted_vals, q):
     return sorted_vals[i]
 
 
-def effective_splits(lens, S, cus):
+def effective_splits(lens, S, cus, groups=1):
     """Most partials any request gets from the library's balanced partition
-    with the MFMA kernel's default grid (one chunk per CU; the rule is stated
-    with the library's split-partition code): requests padded to 32 tokens are
-    laid end to end and cut into G chunks of Q tokens, Q a multiple of 32 and
-    at least ceil(n32_max / (S - 1))."""
+    with the MFMA kernel's default grid (the rule is stated with the
+    library's split-partition code): requests padded to 32 tokens are laid
+    end to end and cut into G = min(CUs / head groups, B (S - 1)) chunks of
+    Q = pad32(ceil(total / G)) tokens."""
     if S == 1:
         return 1
     pad = [-(-n // 32) * 32 for n in lens]
-    total, n32max, G = sum(pad), max(pad), cus
-    Q = max(-(-total // G), -(-n32max // (S - 1)))
-    Q = max(32, -(-Q // 32) * 32)
+    total = sum(pad)
+    G = max(1, min(cus // groups, len(lens) * (S - 1)))
+    Q = max(32, -(-(-(-total // G)) // 32) * 32)
     start, most = 0, 0
     for n, p in zip(lens, pad):
         if n > 0:

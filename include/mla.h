@@ -91,9 +91,10 @@ int mla_num_kv_splits(int64_t max_seq_len, int num_cus, int batch_invariant);
  * Bytes of the fp32 split workspace: B * H * num_kv_splits * (kv_lora_rank + 1)
  * values, the size of the pages' [B, H, num_kv_splits, kv_lora_rank + 1]
  * workspace, holding per (request, head, split) the normalised partial output
- * and its natural-log LSE.  This library stores the partial outputs as rows
- * [B, H, num_kv_splits, kv_lora_rank] followed by the LSEs
- * [B, H, num_kv_splits], so that every row starts on a cache line.
+ * and its natural-log LSE.  This library uses it as a pool of
+ * B * num_kv_splits partial slots per head: partial rows
+ * [H, B * num_kv_splits, kv_lora_rank] followed by the LSEs
+ * [H, B * num_kv_splits], so that every row starts on a cache line.
  * [ESSAY: Data flow (attn_logits shape, the "+1" LSE slot);
  * API: _reserve_attn_logits_workspace sizes it once at the worst case]
  * Host-only.  Returns 0 if any argument is < 1.
@@ -256,12 +257,14 @@ int mla_linear_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, int 
  * outputs and LSEs into `workspace` (fp32; layout at
  * mla_decode_workspace_bytes); stage 2 merges each request's partials by
  * their LSEs.
- * num_kv_splits bounds the number of partials per request and sets the
- * workspace shape.  With num_kv_splits == 1 every request is one partial,
- * reduced in a fixed order independent of the rest of the batch (batch-
- * invariant mode, [ESSAY: Data flow]).  With num_kv_splits > 1 the library
- * partitions each request into at most num_kv_splits contiguous token ranges
- * chosen to balance the whole batch across the GPU's compute units.
+ * num_kv_splits sets the workspace size: B * num_kv_splits partials.  With
+ * num_kv_splits == 1 every request is one partial, reduced in a fixed order
+ * independent of the rest of the batch (batch-invariant mode, [ESSAY: Data
+ * flow]).  With num_kv_splits > 1 the library cuts the whole batch into
+ * equal token chunks across the GPU's compute units; each piece of a request
+ * inside a chunk is one partial, and a long request may take more than
+ * num_kv_splits of the B * num_kv_splits slots when shorter requests leave
+ * them free.
  *
  *   q, q_stride_b, q_stride_h : [B, H, R + P], strides in elements, innermost
  *                               dimension contiguous

@@ -260,6 +260,12 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
     int g = cus * per_cu / groups;
     p.G = g < 1 ? 1 : g;
   }
+  // balanced: the chunks' partials must fit the B * S slots of the workspace
+  // (slot of chunk c, request b is c + b)
+  if (p.partition == PART_BALANCED) {
+    const long long cap = (long long)B * (num_kv_splits - 1);
+    if (p.G > cap) p.G = (int)cap;
+  }
 
   (void)hipGetLastError();
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

@@ -311,7 +311,7 @@ struct Stage1 {
       TileLoad<R, NW>::tile(p, tile_start, se, pg0, buf, buf + (G::CHUNKS / 8 - 1) * 4096, s_table, wave, lane);
   }
 
-  // Token range [a, e) of request b for this wave's heads; writes partial `part`.
+  // Token range [a, e) of request b for this wave's heads; writes partial slot `part`.
   static __device__ void piece(const DecodeParams& p, int b, int a, int e, int part, int head0,
                                char* smem, int* s_table, int* s_flags) {
     const int lane = threadIdx.x & 63;
@@ -556,11 +556,11 @@ struct Stage1 {
       const float inv = kvs / lm;
       const float lse = (m_ref[nb] + __builtin_amdgcn_logf(l)) * kLn2;
       const int h = head0 + 16 * nb + r16;
-      float* dst = ws_row(p, b, h, part, R);
+      float* dst = ws_row(p, part, h, R);
 #pragma unroll
       for (int cb = 0; cb < G::CB; ++cb)
         *reinterpret_cast<f32x4_t*>(dst + 16 * cb + 4 * g) = acc[cb][nb] * inv;
-      if (g == 0) *ws_lse(p, b, h, part, R) = lse;
+      if (g == 0) *ws_lse(p, part, h, R) = lse;
     }
   }
 };
@@ -607,7 +607,7 @@ __global__ __launch_bounds__(K::NW_ * 64) void stage1_mfma_kernel(DecodeParams p
     lo = item;   // the single (request, split) of this workgroup
   } else {
     const BatchTotals t = batch_totals(p.seq_lens, p.B, lane);
-    Q = balanced_chunk(t, p.G, p.S);
+    Q = balanced_chunk(t, p.G);
     lo = (long long)item * Q;
     hi = min(lo + Q, t.total);
     done = lo >= hi;
@@ -618,10 +618,11 @@ __global__ __launch_bounds__(K::NW_ * 64) void stage1_mfma_kernel(DecodeParams p
     if (literal) {
       done = true;
       b = item / p.S;
-      part = item - b * p.S;
+      const int s = item - b * p.S;
+      part = item;                         // slot b * S + s
       const int n = p.seq_lens[b];
       const int kps = (n + p.S - 1) / p.S;
-      a = part * kps;
+      a = s * kps;
       e = min(a + kps, n);
       if (n <= 0 || e <= a) break;
     } else {
@@ -644,7 +645,7 @@ __global__ __launch_bounds__(K::NW_ * 64) void stage1_mfma_kernel(DecodeParams p
       b = base + j;
       a = (int)(lo > st ? lo - st : 0);
       e = (int)min(hi - st, (long long)nn);
-      part = (int)(item - st / Q);
+      part = item + b;                     // slot of the piece (chunk item, request b)
     }
     // the piece is the same for every lane: say so, so that its bounds and
     // loop counters live in scalar registers

@@ -115,8 +115,8 @@ __device__ void valu_piece(const DecodeParams& p, int b, int h0, int a, int e, i
       o += sm_acc[w][hh][d] * c;
     }
     if (h < p.H) {
-      ws_row(p, b, h, part, R)[d] = o / L * kvs;
-      if (d == 0) *ws_lse(p, b, h, part, R) = M + logf(L);
+      ws_row(p, part, h, R)[d] = o / L * kvs;
+      if (d == 0) *ws_lse(p, part, h, R) = M + logf(L);
     }
   }
   __syncthreads();   // LDS is reused by the next piece
@@ -138,14 +138,14 @@ __global__ __launch_bounds__(kWave * kValuWaves) void stage1_valu_kernel(DecodeP
     const int a = s * kps;
     const int e = min(a + kps, n);
     if (e <= a) return;
-    valu_piece<QT, CT, R, P>(p, b, h0, a, e, s, sm_acc, sm_ml);
+    valu_piece<QT, CT, R, P>(p, b, h0, a, e, b * p.S + s, sm_acc, sm_ml);
     return;
   }
 
   // balanced: workgroup blockIdx.x owns chunk [g*Q, (g+1)*Q) of the padded line
   const int g = blockIdx.x;
   const BatchTotals t = batch_totals(p.seq_lens, p.B, lane);
-  const long long Q = balanced_chunk(t, p.G, p.S);
+  const long long Q = balanced_chunk(t, p.G);
   const long long lo = (long long)g * Q;
   const long long hi = min(lo + Q, t.total);
   if (lo >= hi) return;
@@ -165,8 +165,7 @@ __global__ __launch_bounds__(kWave * kValuWaves) void stage1_valu_kernel(DecodeP
       const int nn = __shfl(n, j, kWave);
       const int a = (int)(lo > st ? lo - st : 0);
       const int e = (int)min(hi - st, (long long)nn);
-      const int part = (int)(g - st / Q);
-      valu_piece<QT, CT, R, P>(p, base + j, h0, a, e, part, sm_acc, sm_ml);
+      valu_piece<QT, CT, R, P>(p, base + j, h0, a, e, g + base + j, sm_acc, sm_ml);   // slot c + b
     }
     carry += __shfl(incl, kWave - 1, kWave);
     if (carry >= hi) break;
@@ -211,17 +210,22 @@ __global__ __launch_bounds__(kWave * kMergeWaves) void stage2_merge_kernel(Decod
   const int h = (blockIdx.x - b * hblocks) * kMergeWaves + wave;
   if (h >= p.H) return;
   const int n = p.seq_lens[b];
-  int k;
+  int k, first;
   if (p.partition == PART_LITERAL) {
     k = literal_num_partials(n, p.S);
+    first = b * p.S;
   } else {
     long long start;
     const BatchTotals t = batch_totals_and_start(p.seq_lens, p.B, b, lane, start);
-    k = balanced_num_partials(start, n, balanced_chunk(t, p.G, p.S));
+    const long long Q = balanced_chunk(t, p.G);
+    k = balanced_num_partials(start, n, Q);
+    first = (int)(start / Q) + b;
   }
   k = __builtin_amdgcn_readfirstlane(k);
-  const f32x4* rows = reinterpret_cast<const f32x4*>(ws_row(p, b, h, 0, R));   // partial s at rows + s R / 4
-  const float* lses = ws_lse(p, b, h, 0, R);
+  first = __builtin_amdgcn_readfirstlane(first);
+  // the request's partials are consecutive slots: partial s at rows + s R / 4
+  const f32x4* rows = reinterpret_cast<const f32x4*>(ws_row(p, first, h, R));
+  const float* lses = ws_lse(p, first, h, R);
   f32x4 acc[V4];
 #pragma unroll
   for (int q = 0; q < V4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};

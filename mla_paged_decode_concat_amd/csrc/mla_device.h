@@ -105,11 +105,19 @@ __device__ __forceinline__ long long wave_scan_i64(long long v, int lane) {
 //   empty splits are skipped, so the non-empty ones are s = 0..ceil(n/kps)-1.
 //
 // BALANCED: the requests, each padded to a multiple of 32 tokens, are laid
-//   end to end; that line is cut into G chunks of Q tokens (Q a multiple of
-//   32), and chunk g is handled by stage-1 workgroup g.  A request's partial
-//   p is the part of it inside chunk (first_chunk(b) + p).  Q is at least
-//   ceil(n32_max / (S - 1)), which keeps every request within S partials
-//   (a request of n32 tokens touches at most floor((n32 - 1) / Q) + 2 chunks).
+//   end to end; that line is cut into G chunks of Q = pad32(ceil(total / G))
+//   tokens, and chunk c is handled by stage-1 workgroup c.  The part of
+//   request b inside chunk c is one partial.
+//
+// Partial slots.  The workspace holds B * S partial rows per head, used as
+// one pool.  LITERAL: split s of request b is slot b * S + s.  BALANCED: the
+// piece (chunk c, request b) is slot c + b.  Walking the line, each next
+// piece has a larger chunk index, a larger request index, or both, so slots
+// are distinct, and a request's pieces occupy consecutive slots
+// [c_first + b, c_last + b].  With G <= B * (S - 1) (the host caps it) every
+// slot is below B * S.  A long request may so take more than S partials when
+// shorter ones leave slots free: the chunk count is bounded by the batch's
+// slot total, not by its longest request.
 // ---------------------------------------------------------------------------
 
 enum : int { PART_LITERAL = 1, PART_BALANCED = 2 };
@@ -139,16 +147,13 @@ __device__ __forceinline__ BatchTotals batch_totals(const int32_t* __restrict__ 
   return t;
 }
 
-__device__ __forceinline__ long long balanced_chunk(const BatchTotals& t, int G, int S) {
-  long long q = (t.total + G - 1) / G;
-  long long qmin = S > 1 ? ((long long)t.n32_max + S - 2) / (S - 1) : (long long)t.n32_max;
-  q = q > qmin ? q : qmin;
-  q = pad32(q);
+__device__ __forceinline__ long long balanced_chunk(const BatchTotals& t, int G) {
+  const long long q = pad32((t.total + G - 1) / G);
   return q > 0 ? q : kChunkAlign;
 }
 
 // Number of partials stage 1 wrote for a request of n tokens whose padded
-// start on the balanced line is `start`.
+// start on the balanced line is `start`; its first slot is start / Q + b.
 __device__ __forceinline__ int balanced_num_partials(long long start, int n, long long Q) {
   if (n <= 0) return 0;
   return (int)((start + n - 1) / Q - start / Q + 1);
@@ -192,7 +197,7 @@ struct DecodeParams {
   long long bt_stride;
   const int32_t* seq_lens;
   const float* kv_scale;           // device scalar (fp8 cache) or null
-  float* ws;                       // partial rows [B, H, S, R], then LSEs [B, H, S]
+  float* ws;                       // partial rows [H, B*S, R], then LSEs [H, B*S]
   void* o;                         // [B, H, R]
   float* lse;                      // [B, H]
   float sm_scale;
@@ -204,14 +209,14 @@ struct DecodeParams {
 };
 
 // Workspace layout (fp32, B*H*S*(R+1) values as the split workspace of the
-// pages): the normalised partial outputs as rows [B, H, S, R] -- each row a
-// multiple of 1 KB, so rows start on cache lines -- followed by their LSEs
-// [B, H, S].
-__device__ __forceinline__ float* ws_row(const DecodeParams& p, int b, int h, int s, int R) {
-  return p.ws + (((long long)b * p.H + h) * p.S + s) * R;
+// pages): the normalised partial outputs as rows [H, B*S, R] -- each row a
+// multiple of 1 KB, so rows start on cache lines, and the slots of one head
+// are consecutive rows -- followed by their LSEs [H, B*S].
+__device__ __forceinline__ float* ws_row(const DecodeParams& p, int slot, int h, int R) {
+  return p.ws + ((long long)h * p.B * p.S + slot) * R;
 }
-__device__ __forceinline__ float* ws_lse(const DecodeParams& p, int b, int h, int s, int R) {
-  return p.ws + (long long)p.B * p.H * p.S * R + ((long long)b * p.H + h) * p.S + s;
+__device__ __forceinline__ float* ws_lse(const DecodeParams& p, int slot, int h, int R) {
+  return p.ws + (long long)p.B * p.H * p.S * R + (long long)h * p.B * p.S + slot;
 }
 
 }  // namespace mla

@@ -264,3 +264,18 @@ def test_fp8_write_every_bf16_pattern():
         ref = O.cache_write(np.full((T, 1, 576), 0x7F, np.uint8), W.bits(kv_c), W.bits(k_pe), slots.cpu().numpy(),
                             "bf16", "fp8", float(np.float32(sc)))
         assert np.array_equal(cache.cpu().numpy(), ref), sc
+
+
+@pytest.mark.parametrize("lens,S,grid", [([5000, 1, 1], 2, 0), ([3000, 40, 0, 900], 3, 0), ([4096] + [7] * 31, 8, 0),
+                                         ([700, 2000], 2, 1000)])
+def test_long_request_takes_free_partial_slots(lens, S, grid):
+    """Balanced partition: the workspace's B*S partial slots are one pool, so
+    a long request next to short ones is cut into more than S pieces (the
+    host caps the chunk count at B*(S-1), also for an explicit grid)."""
+    bt = W.make_batch(2, DEV, seq_lens=lens)
+    ref_cache = oracle_cache(bt)
+    _write(bt)
+    o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
+    for kernel in [1, 2]:
+        o, lse = _decode(bt, S, kernel=kernel, partition=2, grid=grid)
+        compare(o, lse, o_ref, lse_ref, "bf16")
