@@ -27,6 +27,19 @@ int device_cu_count() {
 
 bool shape_supported(int R, int P) { return (R == 512 && P == 64) || (R == 256 && P == 64); }
 
+int g_lds_per_cu[kMaxDevices];   // 0 = not queried yet
+
+int device_lds_per_cu() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 160 * 1024;
+  int n = __atomic_load_n(&g_lds_per_cu[dev], __ATOMIC_RELAXED);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess || n < 1)
+    n = 160 * 1024;
+  __atomic_store_n(&g_lds_per_cu[dev], n, __ATOMIC_RELAXED);
+  return n;
+}
+
 int elem_bytes(int dt) { return dt == MLA_F32 ? 4 : dt == MLA_BF16 ? 2 : 1; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -254,9 +267,11 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
   if (op.grid) {
     p.G = op.grid;
   } else {
-    // one resident workgroup per compute unit for the MFMA kernel (its LDS
-    // pipeline fills the CU); the vector kernel runs four per CU
-    const int per_cu = use_mfma ? 1 : 4;
+    // as many MFMA workgroups per compute unit as fit at once (one for the
+    // 64- and 128-head shapes, whose tile ring fills the LDS; two or three of
+    // the one-wave shapes); the vector kernel runs four per CU
+    const int per_cu =
+        use_mfma ? mfma_wgs_per_cu(p.heads_per_group, kv_lora_rank, cache_dtype, device_lds_per_cu()) : 4;
     int g = cus * per_cu / groups;
     p.G = g < 1 ? 1 : g;
   }

@@ -676,11 +676,40 @@ int mfma_heads_per_group(int H, int S) {
   return 16;
 }
 
-// deepest pipeline whose wait count fits the 6-bit vmcnt field
+// Pipeline depth.  A one-wave workgroup (16 or 32 heads) keeps two tiles in
+// its ring, so that several such workgroups share a CU (their waves land on
+// different SIMDs and hide each other's load stalls); wider workgroups take
+// the deepest ring whose wait count fits the 6-bit vmcnt field.
 template <int R, int NW, bool F8>
 constexpr int stages_for() {
   constexpr int lpw = F8 ? TileLoad8<R, NW>::LPW : Geo<R>::NBLK / NW;
+  if constexpr (NW == 1 && !F8) return 2;
   return (2 * lpw < 64) ? 4 : 3;
+}
+
+template <class K>
+constexpr int lds_bytes() { return K::SMEM + K::TABLE * (int)sizeof(int) + 2 * (int)sizeof(int); }
+
+template <int R, bool F8>
+static int lds_bytes_r(int hpg) {
+  switch (hpg) {
+    case 128: return lds_bytes<Stage1<R, 2, 4, stages_for<R, 4, F8>(), F8>>();
+    case 64: return lds_bytes<Stage1<R, 2, 2, stages_for<R, 2, F8>(), F8>>();
+    case 32: return lds_bytes<Stage1<R, 2, 1, stages_for<R, 1, F8>(), F8>>();
+    default: return lds_bytes<Stage1<R, 1, 1, stages_for<R, 1, F8>(), F8>>();
+  }
+}
+
+// Workgroups of a head-group size that fit one CU at once: LDS-bound, and at
+// most one wave per SIMD (each wave takes the whole register file share).
+int mfma_wgs_per_cu(int hpg, int R, int cache_dtype, int lds_per_cu) {
+  const bool f8 = cache_dtype == DT_FP8;
+  const int lds = R == 512 ? (f8 ? lds_bytes_r<512, true>(hpg) : lds_bytes_r<512, false>(hpg))
+                           : (f8 ? lds_bytes_r<256, true>(hpg) : lds_bytes_r<256, false>(hpg));
+  const int waves = hpg >= 128 ? 4 : hpg == 64 ? 2 : 1;
+  int n = lds_per_cu / lds;
+  if (n > 4 / waves) n = 4 / waves;
+  return n < 1 ? 1 : n;
 }
 
 template <class K>

@@ -65,5 +65,6 @@ hipError_t launch_shard_merge(int dtype, int R, const void* o_parts, const float
 int mfma_heads_per_group(int H, int S);
 bool mfma_group_ok(int heads_per_group);
 bool mfma_supported(int H, int R, int cache_dtype);
+int mfma_wgs_per_cu(int heads_per_group, int R, int cache_dtype, int lds_per_cu);
 
 }  // namespace mla
