@@ -112,6 +112,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(size_t)MLA_LDS(const char, p);
 }
 
+typedef int v2i32_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// 8 E4M3 codes (bytes of w0, then w1) -> 8 bf16, exactly: an E4M3 value has
+// 4 significant bits, and the conversion's scale is 1
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1
 template <class F, int... I>
 __device__ __forceinline__ void static_for_(F&& f, std::integer_sequence<int, I...>) {
@@ -181,14 +194,16 @@ struct TileLoad {
 
 // fp8 E4M3 cache tiles.  A 32-token tile holds, per token quarter tq, the
 // value columns as R/128 full blocks (cq8, tq) of 8 tokens x 128 bytes at
-// (4 cq8 + tq) * 1024 (token t8, 16-byte chunk c8 at slot 8 t8 + c8), and
-// the 64 rope bytes as a half block at ROPE_OFF + tq * 512 (token t8, chunk y
-// at slot 4 t8 + y).  Loads of a full block are one LDS-DMA instruction
-// (each 8-lane group reads one 128-byte line); the rope half block is one
+// (4 cq8 + tq) * 1024 (token t8, 16-byte chunk c8 at slot 8 t8 + (c8 ^ t8)),
+// and the 64 rope bytes as a half block at ROPE_OFF + tq * 512 (token t8,
+// chunk y at slot 4 t8 + ((y + t8 / 2) & 3)).  The swizzles spread the 8
+// tokens of a block over all eight 16-byte bank groups for both read
+// patterns below.  Loads of a full block are one LDS-DMA instruction (each
+// 8-lane group reads one 128-byte line); the rope half block is one
 // instruction with the upper 32 lanes masked off (their LDS destinations
-// would lie past the half block).  After the tile barrier the waves convert
-// the tile to the bf16 tile layout of TileLoad (fp8 -> fp32 -> bf16 is exact),
-// and the bf16 stage-1 code runs on that.
+// would lie past the half block).  The matrix cores read the fp8 tile
+// directly: K fragments as 16 contiguous bytes per lane, V^T fragments with
+// the 8-bit transpose read, each converted to bf16 in registers (exactly).
 template <int R, int NW>
 struct TileLoad8 {
   static constexpr int D = R + 64;
@@ -217,8 +232,11 @@ struct TileLoad8 {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       const int tq = wave + NW * j;
-      rw.full[j] = row_ptr(p, tile_start + 8 * tq + (lane >> 3), se, pg0, s_table) + (lane & 7) * 16;
-      rw.rope[j] = row_ptr(p, tile_start + 8 * tq + ((lane & 31) >> 2), se, pg0, s_table) + R + (lane & 3) * 16;
+      // lane i fills slot i: token i / 8, chunk (i % 8) ^ token
+      rw.full[j] = row_ptr(p, tile_start + 8 * tq + (lane >> 3), se, pg0, s_table) + ((lane & 7) ^ (lane >> 3)) * 16;
+      // rope lane i < 32 fills slot i: token t = i / 4, chunk (i % 4 - t / 2) & 3
+      const int tr = (lane & 31) >> 2;
+      rw.rope[j] = row_ptr(p, tile_start + 8 * tq + tr, se, pg0, s_table) + R + (((lane & 3) - (tr >> 1)) & 3) * 16;
     }
     return rw;
   }
@@ -238,41 +256,6 @@ struct TileLoad8 {
     static_for<LPW>([&](auto i) { issue<decltype(i)::value>(rw, buf, wave, lane); });
   }
 
-  // fp8 tile in `src` -> bf16 tile (TileLoad layout) in `dst`: this wave's quarters
-  static __device__ __forceinline__ void convert(const char* src, char* dst, int wave, int lane) {
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      const int tq = wave + NW * j;
-#pragma unroll
-      for (int it = 0; it < (8 * CPR + 63) / 64; ++it) {
-        const int id = lane + 64 * it;
-        if (id < 8 * CPR) {
-          const int t8 = id / CPR, c = id - t8 * CPR;
-          const char* from = c < 8 * FG ? src + (4 * (c >> 3) + tq) * 1024 + (8 * t8 + (c & 7)) * 16
-                                        : src + ROPE_OFF + tq * 512 + (4 * t8 + (c - 8 * FG)) * 16;
-          const u32x4_t w = *MLA_LDS(const u32x4_t, from);
-          const uint32_t wd[4] = {w[0], w[1], w[2], w[3]};
-          uint32_t o[8];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[q], false);   // bytes 0, 1
-            const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[q], true);    // bytes 2, 3
-            // upper halves of the fp32 values: exact bf16 (an E4M3 value has 4 significant bits)
-            o[2 * q] = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u);
-            o[2 * q + 1] = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u);
-          }
-          // 16 values = bf16 chunks 2c and 2c + 1
-          const int sw = TileLoad<R, NW>::swz(t8, tq);
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int cb = 2 * c + h, cq8 = cb >> 3, c8 = cb & 7;
-            *MLA_LDS(u32x4_t, dst + (4 * cq8 + tq) * 1024 + (8 * t8 + (c8 ^ sw)) * 16) =
-                u32x4_t{o[4 * h], o[4 * h + 1], o[4 * h + 2], o[4 * h + 3]};
-          }
-        }
-      }
-    }
-  }
 };
 
 template <int R, int NB, int NW, int STAGES, bool F8 = false>
@@ -285,10 +268,9 @@ struct Stage1 {
   static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
   static constexpr int HPG = 16 * NB * NW;         // heads per workgroup
   static constexpr int NW_ = NW;
-  // ring slot per tile in flight; an fp8 cache adds one bf16 work tile
+  // ring slot per tile in flight
   static constexpr int SLOT = F8 ? TL8::TILE_BYTES : G::TILE_BYTES;
-  static constexpr int WORK_OFF = STAGES * SLOT;
-  static constexpr int SMEM = STAGES * SLOT + (F8 ? G::TILE_BYTES : 0);
+  static constexpr int SMEM = STAGES * SLOT;
   static constexpr int TABLE = kTableWindow;       // block-table window staged in LDS
 
   // wait until the loads of the tile that has `after` newer tiles in flight landed
@@ -323,14 +305,19 @@ struct Stage1 {
     // an fp8 cache stores row / kv_scale: the scale goes into the scores and the output
     const float kvs = F8 ? *p.kv_scale : 1.0f;
     // ---- Q^T operand in registers: lane = head r16 of block nb, dims 32ks + 8g .. +8
+    // (fp8 cache: k-step pair kp = ks / 2 covers dims 64kp .. +64, of which
+    // lane group g takes 64kp + 16g .. +16, half ks % 2 in k-step ks -- the
+    // K fragments then come from 16 contiguous bytes per lane)
     bf16x8_t qf[NB][G::KS];
     const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + (long long)b * p.q_sb;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int h = head0 + 16 * nb + r16;     // head groups divide H: always a real head
 #pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks)
-        qf[nb][ks] = *reinterpret_cast<const bf16x8_t*>(qb + (long long)h * p.q_sh + 32 * ks + 8 * g);
+      for (int ks = 0; ks < G::KS; ++ks) {
+        const int d = F8 ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : 32 * ks + 8 * g;
+        qf[nb][ks] = *reinterpret_cast<const bf16x8_t*>(qb + (long long)h * p.q_sh + d);
+      }
     }
     // Q has landed before the tile loop starts: without this the compiler
     // guards each first use of Q inside the loop with a vmcnt wait, which
@@ -426,12 +413,6 @@ struct Stage1 {
             issue_tile(p, sa + kTile * (t + STAGES - 1), se, pg0, smem + ((t + STAGES - 1) % STAGES) * SLOT,
                        s_table, wave, lane);
           const char* tile = smem + (t % STAGES) * SLOT;
-          if constexpr (F8) {
-            // every wave is past tile t-1's reads of the work tile (barrier above)
-            TL8::convert(tile, smem + WORK_OFF, wave, lane);
-            __syncthreads();   // the bf16 work tile is complete
-            tile = smem + WORK_OFF;
-          }
           const int tile_start = sa + kTile * t;
 
           // ---- S^T = K Q^T  (2 token blocks x NB head blocks); K rows read two
@@ -441,27 +422,67 @@ struct Stage1 {
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) s[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          bf16x8_t kr[3][2];
+          if constexpr (!F8) {
+            bf16x8_t kr[3][2];
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-              kr[ks][mb] = *MLA_LDS(const bf16x8_t, tile + ((ks >> 1) * 4 + 2 * mb) * 1024 + k_off[ks & 1]);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int ks = 0; ks < G::KS; ++ks) {
-            if (ks + 2 < G::KS) {
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
               for (int mb = 0; mb < 2; ++mb)
-                kr[(ks + 2) % 3][mb] =
-                    *MLA_LDS(const bf16x8_t, tile + (((ks + 2) >> 1) * 4 + 2 * mb) * 1024 + k_off[ks & 1]);
-            }
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-              for (int nb = 0; nb < NB; ++nb)
-                s[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks % 3][mb], qf[nb][ks], s[mb][nb], 0, 0, 0);
+                kr[ks][mb] = *MLA_LDS(const bf16x8_t, tile + ((ks >> 1) * 4 + 2 * mb) * 1024 + k_off[ks & 1]);
             __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < G::KS; ++ks) {
+              if (ks + 2 < G::KS) {
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+                  kr[(ks + 2) % 3][mb] =
+                      *MLA_LDS(const bf16x8_t, tile + (((ks + 2) >> 1) * 4 + 2 * mb) * 1024 + k_off[ks & 1]);
+              }
+#pragma unroll
+              for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                  s[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks % 3][mb], qf[nb][ks], s[mb][nb], 0, 0, 0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {
+            // K fragments straight from the fp8 tile: for k-step pair kp and
+            // token block mb, lane (token r16, group g) reads the 16 bytes of
+            // dims 64kp + 16g .. +16 and converts them to the bf16 fragments
+            // of k-steps 2kp and 2kp + 1; reads run one pair ahead
+            constexpr int KP = G::KS / 2;
+            constexpr int VP = R / 64;                // pairs in the value columns
+            const int t8 = r16 & 7;
+            auto kread = [&](int kp, int mb) -> u32x4_t {
+              const int tq = 2 * mb + (r16 >> 3);
+              const char* a = kp < VP
+                                  ? tile + (4 * (kp >> 1) + tq) * 1024 + (8 * t8 + ((4 * (kp & 1) + g) ^ t8)) * 16
+                                  : tile + TL8::ROPE_OFF + tq * 512 + (4 * t8 + ((g + (t8 >> 1)) & 3)) * 16;
+              return *MLA_LDS(const u32x4_t, a);
+            };
+            u32x4_t kw[2][2];
+            kw[0][0] = kread(0, 0);
+            kw[0][1] = kread(0, 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kp = 0; kp < KP; ++kp) {
+              if (kp + 1 < KP) {
+                kw[(kp + 1) & 1][0] = kread(kp + 1, 0);
+                kw[(kp + 1) & 1][1] = kread(kp + 1, 1);
+              }
+#pragma unroll
+              for (int mb = 0; mb < 2; ++mb) {
+                const u32x4_t w = kw[kp & 1][mb];
+                const bf16x8_t k0 = fp8x8_to_bf16(w[0], w[1]);
+                const bf16x8_t k1 = fp8x8_to_bf16(w[2], w[3]);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                  s[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[nb][2 * kp], s[mb][nb], 0, 0, 0);
+                  s[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[nb][2 * kp + 1], s[mb][nb], 0, 0, 0);
+                }
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
 
           // ---- softmax in the log2 domain; lane owns head r16, tokens 16mb + 4g + i
@@ -515,24 +536,52 @@ struct Stage1 {
 
           // ---- O^T += V^T P^T  (CB column blocks x NB head blocks); V^T read
           // two column blocks ahead through a 3-slot ring
-          auto vread = [&](int cb) -> bf16x8_t {
-            const char* vb = tile + (cb >> 2) * 4096 + v_off[cb & 3];
-            const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(MLA_LDS(bf16x4_t, vb));
-            const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(MLA_LDS(bf16x4_t, vb + 2048));
-            return bf16x8_t{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-          };
-          __builtin_amdgcn_sched_barrier(0);
-          bf16x8_t vr[3];
-          vr[0] = vread(0);
-          vr[1] = vread(1);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int cb = 0; cb < G::CB; ++cb) {
-            if (cb + 2 < G::CB) vr[(cb + 2) % 3] = vread(cb + 2);
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-              acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[cb % 3], pf[nb], acc[cb][nb], 0, 0, 0);
+          if constexpr (!F8) {
+            auto vread = [&](int cb) -> bf16x8_t {
+              const char* vb = tile + (cb >> 2) * 4096 + v_off[cb & 3];
+              const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(MLA_LDS(bf16x4_t, vb));
+              const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(MLA_LDS(bf16x4_t, vb + 2048));
+              return bf16x8_t{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            };
             __builtin_amdgcn_sched_barrier(0);
+            bf16x8_t vr[3];
+            vr[0] = vread(0);
+            vr[1] = vread(1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int cb = 0; cb < G::CB; ++cb) {
+              if (cb + 2 < G::CB) vr[(cb + 2) % 3] = vread(cb + 2);
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb)
+                acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[cb % 3], pf[nb], acc[cb][nb], 0, 0, 0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {
+            // V^T fragments by the 8-bit transpose read: in lane group g,
+            // source lane r16 = 2i + hh names the token bound to k-slot i
+            // ({4g .. 4g+3, 16+4g .. 16+4g+3}) and byte half hh of a 16-column
+            // block; lane (g, c) gets column c of those 8 tokens
+            const int i8 = r16 >> 1, hh = r16 & 1;
+            const int tok = i8 < 4 ? 4 * g + i8 : 12 + 4 * g + i8;
+            const int tqv = tok >> 3, t8v = tok & 7;
+            auto vread8 = [&](int cb) -> v2i32_t {
+              const char* a = tile + (4 * (cb >> 3) + tqv) * 1024 + (8 * t8v + ((cb & 7) ^ t8v)) * 16 + 8 * hh;
+              return __builtin_amdgcn_ds_read_tr8_b64_v2i32(MLA_LDS(v2i32_t, a));
+            };
+            __builtin_amdgcn_sched_barrier(0);
+            v2i32_t vw[3];
+            vw[0] = vread8(0);
+            vw[1] = vread8(1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int cb = 0; cb < G::CB; ++cb) {
+              if (cb + 2 < G::CB) vw[(cb + 2) % 3] = vread8(cb + 2);
+              const bf16x8_t vf = fp8x8_to_bf16((uint32_t)vw[cb % 3][0], (uint32_t)vw[cb % 3][1]);
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb)
+                acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[nb], acc[cb][nb], 0, 0, 0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
         }
         if (!redo) {
