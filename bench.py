@@ -147,6 +147,22 @@ def main():
     bulk_bytes = N * (D * 2 + D * 2 + 8)
     bulk_gbs = bulk_bytes / (statistics.median(bulk_ms) * 1e-3) / 1e9
 
+    def timed_us(fn, n=10):
+        """GPU time per call: the stream is held by a spin kernel while
+        the n calls are queued behind the start event, so host-side
+        launch overhead does not show as idle time between them."""
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(5_000_000)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
     # per-step inputs: the newest token of every request
     idx = bt.last_token_rows
     step_kv_c = bt.kv_c.index_select(0, idx).contiguous()
@@ -156,6 +172,8 @@ def main():
     o = torch.empty((B, H, R), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     kw = dict(kernel=args.kernel, grid=args.grid, heads_per_group=args.heads_per_group, partition=args.partition)
+    # the per-step write of the B new tokens alone (GPU time)
+    step_write_us = timed_us(lambda: M.cache_write(step_kv_c, step_k_pe, bt.cache, step_slots, "auto"), n=20)
 
     def step(S_, evs=None):
         M.cache_write(step_kv_c, step_k_pe, bt.cache, step_slots, "auto")
@@ -212,22 +230,6 @@ def main():
     extras = None
     if not args.main_only:
         # the rows beyond the single-token step, each timed on its own with events
-        def timed_us(fn, n=10):
-            """GPU time per call: the stream is held by a spin kernel while
-            the n calls are queued behind the start event, so host-side
-            launch overhead does not show as idle time between them."""
-            for _ in range(3):
-                fn()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            torch.cuda._sleep(5_000_000)
-            a.record()
-            for _ in range(n):
-                fn()
-            b.record()
-            torch.cuda.synchronize()
-            return a.elapsed_time(b) * 1e3 / n
-
         # non-causal multi-token decode: 2 query tokens per request on the same
         # cache, run as 2*H rows of one request
         q2 = W.multi_token_q(bt, 2)
@@ -261,6 +263,7 @@ def main():
                                                        positions=step_pos, cos_sin_cache=tab),
                                          M.rope_q(qr, step_pos, tab, R)), n=20)
         del qr
+        M.cache_write(bt.kv_c, bt.k_pe, bt.cache, bt.slot_mapping, "auto")   # back to the unrotated cache
         # absorbed projections at the DeepSeek-V3 per-GPU shape, batch 64:
         # q_c [64, 1536] x W_Q_UK^T -> [64, 128*512]; o [64, 128*512] x W_UV_O^T -> [64, 7168]
         gq = torch.Generator(device=dev).manual_seed(7)
@@ -345,6 +348,7 @@ def main():
         "mfma_frac": round(mfma_tflops / BF16_PEAK_TFLOPS, 4),
         "hbm_floor_us": round(kv_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
         "bulk_write_gbps": round(bulk_gbs, 1),
+        "step_cache_write_us": round(step_write_us, 2),
         "batch_invariant_us_per_step": round(inv_us, 2) if inv_us else None,
         "decode_us_p10_p50_p90": [round(pct(dec_us, q), 2) for q in (10, 50, 90)],
         "decode_us_llc_flushed_p10_p50_p90": [round(pct(fl_us, q), 2) for q in (10, 50, 90)] if fl_us else None,
@@ -401,6 +405,8 @@ def cpu_baseline(bt, step_kv_c, step_k_pe, step_slots, seconds):
     t0 = time.perf_counter()
     cache = O.cache_write(cache, skv, skp, ssl, spec.in_dtype, spec.cache_dtype)
     t_write = time.perf_counter() - t0
+    # the GPU cache after every timed step, copied back, against the oracle's write
+    write_exact = bool(np.array_equal(W.bits(bt.cache), cache))
     t0 = time.perf_counter()
     done = 0
     for b in range(bt.B):
@@ -416,6 +422,7 @@ def cpu_baseline(bt, step_kv_c, step_k_pe, step_slots, seconds):
         "unit": "us/step",
         "cores": int(threads),
         "kind": "oracle",
+        "gpu_cache_write_bit_exact": write_exact,
         "sample": f"oracle per-step write of {bt.B} tokens + fp64 decode of {done} of {bt.B} requests "
                   f"(8192 tokens x 128 heads each), time scaled to {bt.B} requests; host os.cpu_count()="
                   f"{os.cpu_count()}",
