@@ -69,14 +69,23 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_v3_b64_h128_n8192_hbm_t
 STAGE1_SOURCES = ["api.hip", "decode_mfma.hip", "mla_device.h", "mla_launch.h"]
 
 
+def code_tokens(text: str) -> str:
+    """C++ source without comments and with whitespace collapsed, so that a
+    comment edit does not count as a kernel change."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_sources_sha256() -> str:
-    """sha256 over the stage-1 kernel's sources (file names and bytes)."""
+    """sha256 over the stage-1 kernel's sources (file names and code)."""
     import hashlib
     h = hashlib.sha256()
     for name in STAGE1_SOURCES:
         h.update(name.encode())
-        with open(os.path.join(ROOT, "mla_paged_decode_concat_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "mla_paged_decode_concat_amd", "csrc", name)) as f:
+            h.update(code_tokens(f.read()).encode())
     return h.hexdigest()
 
 

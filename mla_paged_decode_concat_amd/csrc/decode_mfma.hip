@@ -12,7 +12,8 @@
 //    KV tile is read from HBM once and shared by every head (the Triton
 //    prior art re-reads it per 16-head group).
 //  * Tiles stream HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging),
-//    STAGES tiles in flight.  Inside a tile, 8 tokens x 128 bytes (full
+//    STAGES tiles in flight; an fp8 cache's tiles are read by the matrix
+//    cores as fp8 and converted to bf16 in registers.  Inside a tile, 8 tokens x 128 bytes (full
 //    cache lines) form one 1 KB block written by one load instruction; the
 //    slot swizzle 8*t + (c ^ (2*(t >> 1) + (tq & 1))) keeps both LDS read
 //    patterns below free of bank conflicts.
@@ -32,8 +33,10 @@
 //    in the accumulation registers).
 //  * Each CU keeps only about 36-40 KB of loads in flight before a further
 //    load issue stalls the issuing wave, so a workgroup gets about one tile
-//    per HBM round trip; the loads of a tile are issued in one burst after
-//    the tile barrier, three tiles ahead.
+//    per HBM round trip; the loads of the tile three ahead are issued in two
+//    parts, after the tile barrier and after QK.
+//  * Workgroups of 16 or 32 heads are one wave with a two-tile ring, several
+//    to a CU (one wave per SIMD), so their stalls and compute overlap.
 //  * The request's block-table slice is staged in LDS, so page lookups are
 //    LDS reads and never wait behind the tile loads on the vmcnt counter.
 //  * Workgroups that share a token range (different head groups) get ids
