@@ -250,8 +250,9 @@ int mla_linear_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, int 
  * passed as H = q_len * heads rows: q [B, q_len, heads, R + P] with
  * q_stride_h the head stride and a token stride of heads * q_stride_h; o and
  * lse then read as [B, q_len, heads, R] and [B, q_len, heads].  The rows of a
- * request are processed together, so each KV tile is read once for all of
- * them rather than once per query token.
+ * request are processed as its heads: a KV tile is read once per group of up
+ * to 128 rows (groups of one token range share it through L2), not once per
+ * query token.
  *
  * Two stages run on `stream`: stage 1 writes per-split normalised partial
  * outputs and LSEs into `workspace` (fp32; layout at
