@@ -257,7 +257,10 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
   const int cus = device_cu_count();
   int groups;   // head groups per token chunk
   if (use_mfma) {
-    p.heads_per_group = op.heads_per_group ? op.heads_per_group : mfma_heads_per_group(H, num_kv_splits);
+    const long long literal_items = p.partition == PART_LITERAL ? (long long)B * num_kv_splits : 0;
+    p.heads_per_group = op.heads_per_group ? op.heads_per_group
+                                           : mfma_heads_per_group(H, kv_lora_rank, cache_dtype, literal_items, cus,
+                                                                  device_lds_per_cu());
     if (!mfma_group_ok(p.heads_per_group) || H % p.heads_per_group != 0) return MLA_ERR_ARG;
     groups = (H + p.heads_per_group - 1) / p.heads_per_group;
   } else {

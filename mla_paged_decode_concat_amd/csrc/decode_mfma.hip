@@ -738,12 +738,18 @@ bool mfma_group_ok(int hpg) { return hpg == 16 || hpg == 32 || hpg == 64 || hpg 
 
 // Heads per workgroup: one workgroup takes up to 128 heads (4 waves of 32)
 // and reads each tile once; the smaller groups exist for head counts that
-// 128 does not divide.
-int mfma_heads_per_group(int H, int S) {
-  (void)S;
-  if (H % 128 == 0) return 128;
-  if (H % 64 == 0) return 64;
-  if (H % 32 == 0) return 32;
+// 128 does not divide.  With the literal partition the work items are fixed
+// (one per request and split), so when they are too few to fill the GPU the
+// heads are split further: the largest group whose workgroups fill every
+// resident slot, else 16 (e.g. batch-invariant decode, one item per request).
+int mfma_heads_per_group(int H, int R, int cache_dtype, long long literal_items, int cus, int lds_per_cu) {
+  int best = H % 128 == 0 ? 128 : H % 64 == 0 ? 64 : H % 32 == 0 ? 32 : 16;
+  if (literal_items <= 0) return best;
+  for (int hpg = best; hpg >= 16; hpg /= 2) {
+    if (H % hpg != 0) continue;
+    const long long wgs = literal_items * (H / hpg);
+    if (wgs >= (long long)cus * mfma_wgs_per_cu(hpg, R, cache_dtype, lds_per_cu)) return hpg;
+  }
   return 16;
 }
 

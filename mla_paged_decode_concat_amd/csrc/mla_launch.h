@@ -62,7 +62,7 @@ hipError_t launch_shard_merge(int dtype, int R, const void* o_parts, const float
                               void* o, float* lse, hipStream_t stream);
 
 // Stage-1 MFMA kernel geometry, needed by the host planner.
-int mfma_heads_per_group(int H, int S);
+int mfma_heads_per_group(int H, int R, int cache_dtype, long long literal_items, int cus, int lds_per_cu);
 bool mfma_group_ok(int heads_per_group);
 bool mfma_supported(int H, int R, int cache_dtype);
 int mfma_wgs_per_cu(int heads_per_group, int R, int cache_dtype, int lds_per_cu);

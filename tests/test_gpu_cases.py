@@ -279,3 +279,14 @@ def test_long_request_takes_free_partial_slots(lens, S, grid):
     for kernel in [1, 2]:
         o, lse = _decode(bt, S, kernel=kernel, partition=2, grid=grid)
         compare(o, lse, o_ref, lse_ref, "bf16")
+
+
+def test_single_split_result_independent_of_head_grouping():
+    """With num_kv_splits = 1 the library picks smaller head groups for small
+    batches; every head's result must not depend on the grouping, so a
+    request decodes to the same bits in any batch."""
+    bt = W.make_batch(2, DEV, seq_lens=[3000, 17, 900], seed=11)
+    _write(bt)
+    outs = [_decode(bt, 1, kernel=2, heads_per_group=hpg) for hpg in [128, 64, 32, 16]]
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
