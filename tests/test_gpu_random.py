@@ -1,0 +1,48 @@
+"""Seeded random decode configurations against the oracle: batch size, head
+count (including counts only the vector kernel takes), lengths (empty, one
+token, ragged, one long request), num_kv_splits, partition and cache type
+drawn per case -- combinations the targeted tests do not enumerate."""
+
+import numpy as np
+import pytest
+import torch
+
+import mla_paged_decode_concat_amd as M
+from mla_paged_decode_concat_amd import workloads as W
+
+from helpers import compare, oracle_cache, oracle_decode
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+SM = W.SM_SCALE
+
+
+def _case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    index = int(rng.choice([1, 2, 3, 4]))
+    B = int(rng.integers(1, 10))
+    H = int(rng.choice([16, 32, 48, 64, 128, 5, 24]))
+    lens = [int(x) for x in rng.integers(0, 1500, B)]
+    if rng.random() < 0.3:
+        lens[int(rng.integers(0, B))] = int(rng.integers(3000, 9000))
+    if rng.random() < 0.3:
+        lens[int(rng.integers(0, B))] = int(rng.choice([0, 1]))
+    S = int(rng.choice([1, 2, 3, 8, 17]))
+    partition = int(rng.choice([0, 1, 2]))
+    return index, H, lens, S, partition
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_configuration_against_oracle(seed):
+    index, H, lens, S, partition = _case(seed)
+    print(f"[random {seed}] workload {index} H={H} S={S} partition={partition} lens={lens}", flush=True)
+    bt = W.make_batch(index, DEV, seq_lens=lens, H=H, seed=seed)
+    ref_cache = oracle_cache(bt)
+    M.cache_write(bt.kv_c, bt.k_pe, bt.cache, bt.slot_mapping, "fp8" if bt.spec.cache_dtype == "fp8" else "auto",
+                  bt.scale)
+    o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
+    o, lse = M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, SM, S, bt.spec.R, kv_scale=bt.scale,
+                      partition=partition)
+    torch.cuda.synchronize()
+    compare(o, lse, o_ref, lse_ref, bt.spec.in_dtype)
