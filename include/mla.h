@@ -8,7 +8,9 @@
  *   [DIFF]  vLLM compare view whose commit is titled "fix TP": files
  *           csrc/cache_kernels.cu, csrc/torch_bindings.cpp,
  *           vllm/attention/ops/triton_decode_attention.py,
- *           vllm/attention/backends/triton_mla.py.
+ *           vllm/attention/backends/triton_mla.py,
+ *           vllm/attention/backends/mla/utils.py,
+ *           vllm/model_executor/models/deepseek_v2.py.
  *   [API]   "vllm.v1.attention.backends.mla.triton_mla" API page,
  *           TritonMLAMetadataBuilder._reserve_attn_logits_workspace.
  *
@@ -52,29 +54,6 @@ enum {
 };
 
 /* Human-readable text for a status code (static storage). */
-/*
- * Merge of partial attention results over disjoint key sets: combining the
- * per-shard outputs of a request whose tokens are split across GPUs (decode
- * context parallelism), here on one GPU's buffers.  For every (b, h):
- *   M = max_g lse_g,   w_g = exp(lse_g - M),
- *   o[b][h][:] = sum_g w_g o_g[b][h][:] / sum_g w_g,   lse[b][h] = M + ln sum_g w_g,
- * the same LSE merge as decode stage 2.  A shard with lse_g = -inf (no keys)
- * contributes nothing; if every shard is empty, o = 0 and lse = -inf.
- * [ESSAY: Design motivation (the decode returns the LSE because the
- *  cross-shard merge relies on it; natural-log LSE); API: DCP all-gathers the
- *  query heads before forward_mqa, so each shard holds every head]
- *   o_parts   : [G, B, H, R] contiguous, element type `dtype`, 16-byte aligned
- *   lse_parts : [G, B, H] contiguous fp32, natural log
- *   dtype     : MLA_F32 or MLA_BF16 (o_parts and o); accumulation is fp32
- *   o         : [B, H, R] contiguous, element type `dtype`, 16-byte aligned
- *   lse       : [B, H] contiguous fp32
- *   R         : 512 or 256
- * Errors: MLA_ERR_ARG (G < 1, B < 0, H < 1, a NULL pointer, misalignment),
- * MLA_ERR_UNSUPPORTED (R, dtype), MLA_ERR_HIP.  B == 0 launches nothing.
- */
-int mla_merge_partials(const void* o_parts, const float* lse_parts, int G, int B, int H, int R, int dtype,
-                       void* o, float* lse, void* stream);
-
 const char* mla_status_string(int status);
 
 /*
@@ -344,6 +323,29 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
                   float* workspace, size_t workspace_bytes,
                   void* o, float* lse, void* stream,
                   const mla_decode_opts_t* opts);
+
+/*
+ * Merge of partial attention results over disjoint key sets: combining the
+ * per-shard outputs of a request whose tokens are split across GPUs (decode
+ * context parallelism), here on one GPU's buffers.  For every (b, h):
+ *   M = max_g lse_g,   w_g = exp(lse_g - M),
+ *   o[b][h][:] = sum_g w_g o_g[b][h][:] / sum_g w_g,   lse[b][h] = M + ln sum_g w_g,
+ * the same LSE merge as decode stage 2.  A shard with lse_g = -inf (no keys)
+ * contributes nothing; if every shard is empty, o = 0 and lse = -inf.
+ * [ESSAY: Design motivation (the decode returns the LSE because the
+ *  cross-shard merge relies on it; natural-log LSE); API: DCP all-gathers the
+ *  query heads before forward_mqa, so each shard holds every head]
+ *   o_parts   : [G, B, H, R] contiguous, element type `dtype`, 16-byte aligned
+ *   lse_parts : [G, B, H] contiguous fp32, natural log
+ *   dtype     : MLA_F32 or MLA_BF16 (o_parts and o); accumulation is fp32
+ *   o         : [B, H, R] contiguous, element type `dtype`, 16-byte aligned
+ *   lse       : [B, H] contiguous fp32
+ *   R         : 512 or 256
+ * Errors: MLA_ERR_ARG (G < 1, B < 0, H < 1, a NULL pointer, misalignment),
+ * MLA_ERR_UNSUPPORTED (R, dtype), MLA_ERR_HIP.  B == 0 launches nothing.
+ */
+int mla_merge_partials(const void* o_parts, const float* lse_parts, int G, int B, int H, int R, int dtype,
+                       void* o, float* lse, void* stream);
 
 #ifdef __cplusplus
 }
