@@ -290,7 +290,9 @@ int mla_decode(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_dtyp
  *                    [DIFF: triton_decode_attention.py, stage 1 split range],
  *                2 = balanced.
  *   kernel     : 0 = default, 1 = the generic vector-ALU stage 1,
- *                2 = the matrix-core (MFMA) stage 1 (bf16 query only).
+ *                2 = the matrix-core (MFMA) stage 1 (bf16 query only),
+ *                3 = the MFMA stage 1 with four waves splitting each token
+ *                range of a 16-head group (bf16 cache, 16 heads per group).
  *   grid       : balanced partition only: number of token chunks the batch
  *                is cut into (0 = derived from the compute-unit count).
  *   heads_per_group : heads handled by one stage-1 workgroup (0 = default).

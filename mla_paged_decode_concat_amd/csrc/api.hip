@@ -198,7 +198,7 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
   mla_decode_opts_t op;
   memset(&op, 0, sizeof(op));
   if (opts) op = *opts;
-  if (op.partition < 0 || op.partition > 2 || op.kernel < 0 || op.kernel > 2 || op.grid < 0 ||
+  if (op.partition < 0 || op.partition > 2 || op.kernel < 0 || op.kernel > 3 || op.grid < 0 ||
       op.heads_per_group < 0)
     return MLA_ERR_ARG;
 
@@ -224,7 +224,7 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
                        (q_stride_b * 2) % 16 == 0 && (q_stride_h * 2) % 16 == 0 &&
                        aligned16(cache) && (block_stride * elem_bytes(cache_dtype)) % 16 == 0;
   bool use_mfma;
-  if (op.kernel == 2) {
+  if (op.kernel == 2 || op.kernel == 3) {
     if (!mfma_ok) return MLA_ERR_UNSUPPORTED;
     use_mfma = true;
   } else if (op.kernel == 1) {
@@ -267,8 +267,28 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
     p.heads_per_group = 4;
     groups = (H + 3) / 4;
   }
+  // 16-head groups: four waves split each token range (kernel 3) instead of
+  // one wave per range.  It pays when ranges are long and too few to give
+  // every CU a one-wave workgroup: by default, the literal partition (whole
+  // requests or ceil(n/S) splits) with at most one range per CU (measured
+  // 2-3x on batch-invariant decode).  Balanced chunks are long or short
+  // depending on the lengths, which the host does not see (16-19% faster for
+  // long ones, 7% slower for a mix of short ones), so there it is opt-in.
+  p.token_split = 0;
+  if (use_mfma && p.heads_per_group == 16) {
+    if (op.kernel == 3) {
+      if (cache_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+      p.token_split = 1;
+    } else if (op.kernel == 0 && cache_dtype == MLA_BF16 && !op.grid && p.partition == PART_LITERAL) {
+      p.token_split = (long long)B * num_kv_splits * groups <= cus ? 1 : 0;
+    }
+  } else if (op.kernel == 3) {
+    return MLA_ERR_UNSUPPORTED;
+  }
   if (op.grid) {
     p.G = op.grid;
+  } else if (p.token_split) {
+    p.G = cus / groups < 1 ? 1 : cus / groups;   // one four-wave workgroup per CU
   } else {
     // as many MFMA workgroups per compute unit as fit at once (one for the
     // 64- and 128-head shapes, whose tile ring fills the LDS; two or three of

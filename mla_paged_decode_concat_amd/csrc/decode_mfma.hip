@@ -636,6 +636,210 @@ struct Stage1 {
   }
 };
 
+// Token-split stage 1 for one 16-head group (bf16 cache).  When the token
+// ranges are few (the partial-slot cap binds, or the literal partition has
+// fewer items than CUs), a one-wave workgroup per range would leave each busy
+// CU with a single load stream.  Here four waves share the range's 16 heads:
+// wave w streams tiles w, w+4, ... into its own LDS slot (its own 32-token
+// tile, loaded by its own 36 instructions and waited on by itself alone),
+// with its own Q copy, accumulators and online softmax (a head's reference
+// moves up when a tile exceeds it by more than kSlack, rescaling that wave's
+// accumulators, which are few enough here to live in vector registers).  At
+// the end the four partial states are merged through LDS into the range's
+// one partial -- the same quantity the other kernels store.
+template <int R>
+struct Stage1TS {
+  using G = Geo<R>;
+  using TL = TileLoad<R, 1>;
+  static constexpr int NW_ = 4;
+  static constexpr int HPG = 16;
+  static constexpr int SLOT = G::TILE_BYTES;
+  static constexpr int SMEM = 4 * SLOT;
+  static constexpr int TABLE = kTableWindow;
+  static constexpr int MERGE_STAT = 4 * 16 * R;     // floats: per-wave accumulators, then statistics
+  static_assert((MERGE_STAT + 4 * 3 * 16) * 4 <= SMEM, "merge area inside the tile slots");
+
+  static __device__ void piece(const DecodeParams& p, int b, int a, int e, int part, int head0,
+                               char* smem, int* s_table, int* s_flags) {
+    (void)s_flags;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int r16 = lane & 15;
+    const int h = head0 + r16;
+
+    bf16x8_t qf[G::KS];
+    const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + (long long)b * p.q_sb + (long long)h * p.q_sh;
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qb + 32 * ks + 8 * g);
+    wait_vmcnt<0>();
+
+    uint32_t k_off[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int t8 = r16 & 7, tqo = r16 >> 3, c8 = 4 * par + g;
+      k_off[par] = (uint32_t)(tqo * 1024 + (8 * t8 + (c8 ^ TL::swz(t8, tqo))) * 16);
+    }
+    uint32_t v_off[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int sg = r16 & 3;
+      const int t8 = 4 * (g & 1) + (r16 >> 2), tqo = g >> 1;
+      const int c8 = 2 * k + (sg >> 1);
+      v_off[k] = (uint32_t)(tqo * 1024 + (8 * t8 + (c8 ^ TL::swz(t8, tqo))) * 16 + (sg & 1) * 8);
+    }
+
+    f32x4_t acc[G::CB];
+#pragma unroll
+    for (int cb = 0; cb < G::CB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_ref = -INFINITY, l_sum = 0.0f, l_mma = 0.0f;
+    const float c2 = p.sm_scale * kLog2e;
+    const int bs = p.block_size;
+    const int32_t* btab = p.block_table + (long long)b * p.bt_stride;
+    char* slot = smem + wave * SLOT;
+
+    for (int sa = a; sa < e;) {
+      const int pg0 = sa / bs;
+      const long long win_end = (long long)(pg0 + kTableWindow) * bs;
+      int se = e;
+      if (win_end < e) se = sa + (int)((win_end - sa) / kTile) * kTile;
+      __syncthreads();   // every wave is done with the previous window's table and its slot
+      const int npg = (se - 1) / bs - pg0 + 1;
+      for (int i = threadIdx.x; i < npg; i += 4 * 64) s_table[i] = btab[pg0 + i];
+      __syncthreads();
+      const int ntiles = (se - sa + kTile - 1) / kTile;
+#pragma unroll 1
+      for (int t = wave; t < ntiles; t += 4) {
+        const int tile_start = sa + kTile * t;
+        TL::tile(p, tile_start, se, pg0, slot, slot + (G::CHUNKS / 8 - 1) * 4096, s_table, 0, lane);
+        wait_vmcnt<0>();   // this wave's own tile; no other wave reads it
+        const char* tile = slot;
+
+        f32x4_t sc[2];
+        sc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        sc[1] = sc[0];
+        bf16x8_t kr[3][2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            kr[ks][mb] = *MLA_LDS(const bf16x8_t, tile + ((ks >> 1) * 4 + 2 * mb) * 1024 + k_off[ks & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) {
+          if (ks + 2 < G::KS) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+              kr[(ks + 2) % 3][mb] =
+                  *MLA_LDS(const bf16x8_t, tile + (((ks + 2) >> 1) * 4 + 2 * mb) * 1024 + k_off[ks & 1]);
+          }
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            sc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks % 3][mb], qf[ks], sc[mb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // online softmax in the log2 domain; lane owns head r16, tokens 16mb + 4g + i
+        float mt = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = tile_start + 16 * mb + 4 * g + i;
+            const float v = tok < se ? sc[mb][i] * c2 : -INFINITY;
+            sc[mb][i] = v;
+            mt = fmaxf(mt, v);
+          }
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const bool up = mt > m_ref + kSlack;     // also true while m_ref is unset
+        if (__builtin_expect(__any(up), 0)) {
+          if (up) {
+            const float f = __builtin_amdgcn_exp2f(m_ref - mt);   // 0 while unset
+#pragma unroll
+            for (int cb = 0; cb < G::CB; ++cb) acc[cb] *= f;
+            l_sum *= f;
+            l_mma *= f;
+            m_ref = mt;
+          }
+        }
+        bf16x8_t pf;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pj = __builtin_amdgcn_exp2f(sc[mb][i] - m_ref);
+            const __bf16 pb = (__bf16)pj;
+            l_sum += pj;
+            l_mma += (float)pb;
+            pf[4 * mb + i] = pb;
+          }
+
+        auto vread = [&](int cb) -> bf16x8_t {
+          const char* vb = tile + (cb >> 2) * 4096 + v_off[cb & 3];
+          const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(MLA_LDS(bf16x4_t, vb));
+          const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(MLA_LDS(bf16x4_t, vb + 2048));
+          return bf16x8_t{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        };
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8_t vr[3];
+        vr[0] = vread(0);
+        vr[1] = vread(1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int cb = 0; cb < G::CB; ++cb) {
+          if (cb + 2 < G::CB) vr[(cb + 2) % 3] = vread(cb + 2);
+          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[cb % 3], pf, acc[cb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      sa = se;
+    }
+
+    // ---- merge the four waves' states into the range's partial
+    l_sum += __shfl_xor(l_sum, 16, 64);
+    l_sum += __shfl_xor(l_sum, 32, 64);
+    l_mma += __shfl_xor(l_mma, 16, 64);
+    l_mma += __shfl_xor(l_mma, 32, 64);
+    __syncthreads();   // every wave is done with its tile slot
+    float* mrg = reinterpret_cast<float*>(smem);
+    float* stat = mrg + MERGE_STAT;
+#pragma unroll
+    for (int cb = 0; cb < G::CB; ++cb)
+      *MLA_LDS(f32x4_t, mrg + ((wave * G::CB + cb) * 64 + lane) * 4) = acc[cb];
+    if (g == 0) {
+      stat[(wave * 3 + 0) * 16 + r16] = m_ref;
+      stat[(wave * 3 + 1) * 16 + r16] = l_sum;
+      stat[(wave * 3 + 2) * 16 + r16] = l_mma;
+    }
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, stat[(w * 3) * 16 + r16]);
+    float wt[4], Ls = 0.0f, Lm = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = stat[(w * 3) * 16 + r16];
+      wt[w] = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);   // a wave without tiles adds nothing
+      Ls += wt[w] * stat[(w * 3 + 1) * 16 + r16];
+      Lm += wt[w] * stat[(w * 3 + 2) * 16 + r16];
+    }
+    const float inv = 1.0f / Lm;
+    float* dst = ws_row(p, part, h, R);
+    constexpr int CPW = G::CB / 4;   // column blocks each wave writes
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      const int cb = wave * CPW + j;
+      f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) o += wt[w] * *MLA_LDS(const f32x4_t, mrg + ((w * G::CB + cb) * 64 + lane) * 4);
+      *reinterpret_cast<f32x4_t*>(dst + 16 * cb + 4 * g) = o * inv;
+    }
+    if (wave == 0 && g == 0) *ws_lse(p, part, h, R) = (M + __builtin_amdgcn_logf(Ls)) * kLn2;
+    __syncthreads();   // the merge area is tile slots again for the next piece
+  }
+};
+
 // Workgroup id -> (work item, head group).  The dispatcher sends id i to XCD
 // i % 8; consecutive items (neighbouring token ranges, which share requests,
 // their queries and block-table rows) are kept on one XCD, and the head
@@ -804,7 +1008,10 @@ static hipError_t launch_r(const DecodeParams& p, hipStream_t stream) {
     case 128: return launch_k<Stage1<R, 2, 4, stages_for<R, 4, F8>(), F8>>(p, stream);
     case 64: return launch_k<Stage1<R, 2, 2, stages_for<R, 2, F8>(), F8>>(p, stream);
     case 32: return launch_k<Stage1<R, 2, 1, stages_for<R, 1, F8>(), F8>>(p, stream);
-    case 16: return launch_k<Stage1<R, 1, 1, stages_for<R, 1, F8>(), F8>>(p, stream);
+    case 16:
+      if constexpr (!F8)
+        if (p.token_split) return launch_k<Stage1TS<R>>(p, stream);
+      return launch_k<Stage1<R, 1, 1, stages_for<R, 1, F8>(), F8>>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -206,6 +206,7 @@ struct DecodeParams {
   int partition;                   // PART_LITERAL | PART_BALANCED
   int G;                           // balanced: chunk count
   int heads_per_group;             // stage 1: heads per workgroup
+  int token_split;                 // stage 1, 16-head groups: four waves split the tokens
 };
 
 // Workspace layout (fp32, B*H*S*(R+1) values as the split workspace of the

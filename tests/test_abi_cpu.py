@@ -120,7 +120,7 @@ def test_decode_validation():
 def test_decode_ex_validation():
     O_ = binding.DecodeOpts
     assert _decode(O_(3, 0, 0, 0)) == -1
-    assert _decode(O_(0, 3, 0, 0)) == -1
+    assert _decode(O_(0, 4, 0, 0)) == -1
     assert _decode(O_(0, 0, -1, 0)) == -1
     assert _decode(O_(0, 2, 0, 0), q_dt=0, cache_dt=0) == -2   # MFMA kernel needs a bf16 query
     assert _decode(O_(0, 0, 0, 0), B=0) == 0

@@ -109,10 +109,10 @@ def test_late_dominant_token_forces_redo():
     _write(bt)
     o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
     assert np.all(lse_ref > 150)
-    for hpg in [32, 128]:
+    for hpg, kernel in [(32, 2), (128, 2), (16, 3)]:
         for S in [1, 4]:
-            _print(f"[redo] hpg={hpg} S={S}")
-            o, lse = _decode(bt, S, kernel=2, heads_per_group=hpg)
+            _print(f"[redo] hpg={hpg} kernel={kernel} S={S}")
+            o, lse = _decode(bt, S, kernel=kernel, heads_per_group=hpg)
             compare(o, lse, o_ref, lse_ref, "bf16")
 
 
@@ -290,3 +290,30 @@ def test_single_split_result_independent_of_head_grouping():
     outs = [_decode(bt, 1, kernel=2, heads_per_group=hpg) for hpg in [128, 64, 32, 16]]
     for o, lse in outs[1:]:
         assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
+
+
+
+@pytest.mark.parametrize("index", [1, 3])
+def test_token_split_kernel(index):
+    """Four waves splitting each token range of a 16-head group (kernel 3):
+    ragged, empty, one-token and long requests, both partitions, several
+    split counts, two head groups, against the oracle."""
+    lens = [0, 1, 31, 33, 700, 2500, 129, 5000]
+    bt = W.make_batch(index, DEV, seq_lens=lens, H=32)    # block 64 (R=512) and block 16 (R=256)
+    ref_cache = oracle_cache(bt)
+    _write(bt)
+    o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
+    for S in [1, 3, 9]:
+        for partition in [1, 2]:
+            _print(f"[ts] workload {index} S={S} partition={partition}")
+            o, lse = _decode(bt, S, kernel=3, heads_per_group=16, partition=partition)
+            compare(o, lse, o_ref, lse_ref, "bf16")
+
+
+def test_token_split_rejects_what_it_cannot_run():
+    bt = W.make_batch(4, DEV, B=2, max_len=300, H=16)     # fp8 cache
+    with pytest.raises(M.MLAError):
+        M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, SM, 2, 512, kv_scale=bt.scale, kernel=3)
+    bt = W.make_batch(1, DEV, B=2, max_len=300, H=32)
+    with pytest.raises(M.MLAError):
+        M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, SM, 2, 512, kernel=3, heads_per_group=32)
