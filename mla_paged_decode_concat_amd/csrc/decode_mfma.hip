@@ -33,8 +33,10 @@
 //    in the accumulation registers).
 //  * Each CU keeps only about 36-40 KB of loads in flight before a further
 //    load issue stalls the issuing wave, so a workgroup gets about one tile
-//    per HBM round trip; the loads of the tile three ahead are issued in two
-//    parts, after the tile barrier and after QK.
+//    per HBM round trip.  With four waves, each issues its loads of the tile
+//    three ahead at its own point of the tile (two inside QK, two inside
+//    PV); narrower workgroups issue theirs in two parts, after the tile
+//    barrier and after QK.
 //  * Workgroups of 16 or 32 heads are one wave with a two-tile ring, several
 //    to a CU (one wave per SIMD), so their stalls and compute overlap.
 //  * The request's block-table slice is staged in LDS, so page lookups are
@@ -288,8 +290,16 @@ struct Stage1 {
   }
 
   static __device__ __forceinline__ int swz(int t8, int tq) { return TileLoad<R, NW>::swz(t8, tq); }
-  // bf16 tiles: load instructions issued before QK; the rest follow QK
+  // bf16 tiles, one or two waves: load instructions issued before QK; the rest follow QK
   static constexpr int kFirst = (LPW * 5 + 8) / 9;
+  // bf16 tiles, four waves: each wave issues all of its loads for the tile
+  // three ahead at its own point of the tile -- waves 0 and 1 at two QK
+  // k-steps, waves 2 and 3 at two PV column blocks -- so that the four
+  // bursts do not queue behind each other at the CU's load unit.  Points are
+  // encoded as 100 + k-step or 300 + column block.
+  static constexpr bool kStagger = !F8 && NW == 4;
+  static constexpr int kIssueAt[4] = {100 + G::KS * 2 / 9, 100 + G::KS * 13 / 18, 300 + G::CB / 4,
+                                      300 + G::CB * 3 / 4};
   template <int I>
   static __device__ __forceinline__ void issue_part(const typename TileLoad<R, NW>::Rows& rw, char* buf, int wave) {
     TileLoad<R, NW>::template issue<I>(rw, buf, buf + (G::CHUNKS / 8 - 1) * 4096, wave);
@@ -427,10 +437,27 @@ struct Stage1 {
           typename TileLoad<R, NW>::Rows nrw;
           if constexpr (F8) {
             if (more) issue_tile(p, sa + kTile * (t + STAGES - 1), se, pg0, nbuf, s_table, wave, lane);
-          } else if (more) {
-            nrw = TileLoad<R, NW>::rows(p, sa + kTile * (t + STAGES - 1), se, pg0, s_table, wave);
-            static_for<kFirst>([&](auto i) { issue_part<decltype(i)::value>(nrw, nbuf, wave); });
+          } else if constexpr (!kStagger) {
+            if (more) {
+              nrw = TileLoad<R, NW>::rows(p, sa + kTile * (t + STAGES - 1), se, pg0, s_table, wave);
+              static_for<kFirst>([&](auto i) { issue_part<decltype(i)::value>(nrw, nbuf, wave); });
+            }
           }
+          // the staggered issue: called at every point, issues in the wave whose point it is
+          auto issue_at = [&](auto P) {
+            constexpr int pt = decltype(P)::value;
+            if constexpr (kStagger) {
+              constexpr int wmask = (kIssueAt[0] == pt ? 1 : 0) | (kIssueAt[1] == pt ? 2 : 0) |
+                                    (kIssueAt[2] == pt ? 4 : 0) | (kIssueAt[3] == pt ? 8 : 0);
+              if constexpr (wmask != 0) {
+                if (more && ((wmask >> wave) & 1)) {
+                  const typename TileLoad<R, NW>::Rows rw =
+                      TileLoad<R, NW>::rows(p, sa + kTile * (t + STAGES - 1), se, pg0, s_table, wave);
+                  static_for<LPW>([&](auto i) { issue_part<decltype(i)::value>(rw, nbuf, wave); });
+                }
+              }
+            }
+          };
           const char* tile = smem + (t % STAGES) * SLOT;
           const int tile_start = sa + kTile * t;
 
@@ -449,8 +476,9 @@ struct Stage1 {
               for (int mb = 0; mb < 2; ++mb)
                 kr[ks][mb] = *MLA_LDS(const bf16x8_t, tile + ((ks >> 1) * 4 + 2 * mb) * 1024 + k_off[ks & 1]);
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int ks = 0; ks < G::KS; ++ks) {
+            static_for<G::KS>([&](auto KSI) {
+              constexpr int ks = decltype(KSI)::value;
+              issue_at(std::integral_constant<int, 100 + ks>{});
               if (ks + 2 < G::KS) {
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
@@ -463,7 +491,7 @@ struct Stage1 {
                 for (int nb = 0; nb < NB; ++nb)
                   s[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks % 3][mb], qf[nb][ks], s[mb][nb], 0, 0, 0);
               __builtin_amdgcn_sched_barrier(0);
-            }
+            });
           } else {
             // K fragments straight from the fp8 tile: for k-step pair kp and
             // token block mb, lane (token r16, group g) reads the 16 bytes of
@@ -504,7 +532,7 @@ struct Stage1 {
             }
           }
 
-          if constexpr (!F8) {
+          if constexpr (!F8 && !kStagger) {
             if (more) static_for<LPW - kFirst>([&](auto i) { issue_part<kFirst + decltype(i)::value>(nrw, nbuf, wave); });
           }
           // ---- softmax in the log2 domain; lane owns head r16, tokens 16mb + 4g + i
@@ -570,14 +598,15 @@ struct Stage1 {
             vr[0] = vread(0);
             vr[1] = vread(1);
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int cb = 0; cb < G::CB; ++cb) {
+            static_for<G::CB>([&](auto CBI) {
+              constexpr int cb = decltype(CBI)::value;
+              issue_at(std::integral_constant<int, 300 + cb>{});
               if (cb + 2 < G::CB) vr[(cb + 2) % 3] = vread(cb + 2);
 #pragma unroll
               for (int nb = 0; nb < NB; ++nb)
                 acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[cb % 3], pf[nb], acc[cb][nb], 0, 0, 0);
               __builtin_amdgcn_sched_barrier(0);
-            }
+            });
           } else {
             // V^T fragments by the 8-bit transpose read: in lane group g,
             // source lane r16 = 2i + hh names the token bound to k-slot i
