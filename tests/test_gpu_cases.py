@@ -248,6 +248,20 @@ def test_batch_invariance_single_split():
         assert torch.equal(o1[0], o[b]) and torch.equal(l1[0], lse[b])
 
 
+def test_batch_invariance_single_split_large_batch():
+    """num_kv_splits = 1 with 16 heads and more requests than compute units:
+    the stage-1 kernel choice must not depend on the batch size, so a request
+    decodes to the same bits alone and inside a batch of 300."""
+    full = W.make_batch(1, DEV, seq_lens=[(37 * i) % 400 + 1 for i in range(300)])
+    _write(full)
+    o, lse = _decode(full, 1)
+    for b in [0, 7, 150, 299]:
+        o1, l1 = M.decode(full.q[b:b + 1].contiguous(), full.cache, full.block_table[b:b + 1].contiguous(),
+                          full.seq_lens[b:b + 1].contiguous(), SM, 1, 512)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0], o[b]) and torch.equal(l1[0], lse[b]), b
+
+
 def test_fp8_write_every_bf16_pattern():
     """All 65536 bf16 bit patterns through the fp8 write, compared with the
     oracle's encoder (covers subnormals, ties, saturation and NaN)."""
