@@ -113,7 +113,7 @@ def parse():
                     help="bound on the CPU oracle's timed work (0 = skip)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
-    ap.add_argument("--kernel", type=int, default=0, help="stage-1 kernel: 0 auto, 1 vector ALU, 2 MFMA")
+    ap.add_argument("--kernel", type=int, default=0, help="stage-1 kernel: 0 auto, 1 vector ALU, 2 MFMA, 3 MFMA token split (16-head groups)")
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--heads-per-group", type=int, default=0)
     ap.add_argument("--partition", type=int, default=0)
