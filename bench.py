@@ -107,8 +107,11 @@ def measured_traffic():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # ~20 ms of untimed steps: the board's clocks take a few hundred steps
+    # to settle (measured: the first 50 steps of a fresh process ran 238 us
+    # against 197 us a few hundred steps later)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="bound on the CPU oracle's timed work (0 = skip)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
