@@ -12,7 +12,9 @@ write of the B new tokens (one per request) followed by the split-KV decode
 
 Prints one JSON line.  Extra fields: per-stage times from HIP events recorded
 on the launch stream, the bulk cache-write bandwidth, the batch-invariant
-(num_kv_splits = 1) step time, and the CPU oracle's time on a bounded sample.
+(num_kv_splits = 1) step time (library default, and with requests of 4096
+tokens or more on the token-split stage 1), and the CPU oracle's time on a
+bounded sample.
 """
 
 import argparse
@@ -58,8 +60,9 @@ class HipEvent:
         return ms.value
 
     def __del__(self):
-        if HipEvent._hip is not None and self.handle:
-            HipEvent._hip.hipEventDestroy(self.handle)
+        hip = type(self)._hip          # module globals may already be gone at interpreter exit
+        if hip is not None and self.handle:
+            hip.hipEventDestroy(self.handle)
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_v3_b64_h128_n8192_hbm_traffic.txt")
@@ -116,7 +119,7 @@ def parse():
                     help="bound on the CPU oracle's timed work (0 = skip)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
-    ap.add_argument("--kernel", type=int, default=0, help="stage-1 kernel: 0 auto, 1 vector ALU, 2 MFMA, 3 MFMA token split (16-head groups)")
+    ap.add_argument("--kernel", type=int, default=0, help="stage-1 kernel: 0 auto, 1 vector ALU, 2 MFMA, 3 MFMA token split (16- or 32-head groups)")
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--heads-per-group", type=int, default=0)
     ap.add_argument("--partition", type=int, default=0)
@@ -224,20 +227,28 @@ def main():
         fl_us = sorted((e[0].ms_until(e[1]) + e[1].ms_until(e[2])) * 1e3 for e in evf)
         del flush
 
-    # batch-invariant run: one split per request
-    inv_us = None
+    # batch-invariant run: one split per request, with the library's default
+    # stage 1 and with requests of 4096 tokens or more on the token-split kernel
+    inv_us = inv_split_us = None
     if not (args.no_invariant or args.main_only):
         ws1 = torch.empty(M.decode_workspace_bytes(B, H, 1, R) // 4, dtype=torch.float32, device=dev)
-        for _ in range(3):
-            M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, W.SM_SCALE, 1, R, workspace=ws1, o=o, lse=lse, **kw)
-        torch.cuda.synchronize()
-        ta = time.perf_counter()
-        n_inv = max(5, K // 5)
-        for _ in range(n_inv):
-            M.cache_write(step_kv_c, step_k_pe, bt.cache, step_slots, "auto")
-            M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, W.SM_SCALE, 1, R, workspace=ws1, o=o, lse=lse, **kw)
-        torch.cuda.synchronize()
-        inv_us = (time.perf_counter() - ta) * 1e6 / n_inv
+
+        def inv_run(split_len):
+            for _ in range(3):
+                M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, W.SM_SCALE, 1, R, workspace=ws1, o=o, lse=lse,
+                         split_len=split_len, **kw)
+            torch.cuda.synchronize()
+            ta = time.perf_counter()
+            n_inv = max(5, K // 5)
+            for _ in range(n_inv):
+                M.cache_write(step_kv_c, step_k_pe, bt.cache, step_slots, "auto")
+                M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, W.SM_SCALE, 1, R, workspace=ws1, o=o, lse=lse,
+                         split_len=split_len, **kw)
+            torch.cuda.synchronize()
+            return (time.perf_counter() - ta) * 1e6 / n_inv
+
+        inv_us = inv_run(0)
+        inv_split_us = inv_run(4096)
 
     extras = None
     if not args.main_only:
@@ -362,6 +373,7 @@ def main():
         "bulk_write_gbps": round(bulk_gbs, 1),
         "step_cache_write_us": round(step_write_us, 2),
         "batch_invariant_us_per_step": round(inv_us, 2) if inv_us else None,
+        "batch_invariant_split_len_4096_us_per_step": round(inv_split_us, 2) if inv_split_us else None,
         "decode_us_p10_p50_p90": [round(pct(dec_us, q), 2) for q in (10, 50, 90)],
         "decode_us_llc_flushed_p10_p50_p90": [round(pct(fl_us, q), 2) for q in (10, 50, 90)] if fl_us else None,
         "num_kv_splits_effective": effective_splits(bt.seq_lens_list, S, cus),

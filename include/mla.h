@@ -292,13 +292,29 @@ int mla_decode(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_dtyp
  *   kernel     : 0 = default, 1 = the generic vector-ALU stage 1,
  *                2 = the matrix-core (MFMA) stage 1 (bf16 query only),
  *                3 = the MFMA stage 1 with four waves splitting each token
- *                range of a 16-head group (bf16 cache, 16 heads per group).
+ *                range of a 16- or 32-head group (bf16 cache; 16 heads per
+ *                group unless heads_per_group is 32).
  *   grid       : balanced partition only: number of token chunks the batch
  *                is cut into (0 = derived from the compute-unit count).
  *   heads_per_group : heads handled by one stage-1 workgroup (0 = default).
  *   stage_events : optional hipEvent_t handles (NULL entries are skipped),
  *                recorded on `stream` before stage 1, between stage 1 and
  *                stage 2, and after stage 2, for timing each stage.
+ *   split_len  : batch-invariant decode (num_kv_splits == 1) of a bf16 cache
+ *                with H a multiple of 32, under the default kernel, grid and
+ *                head grouping: if positive, requests of at least split_len
+ *                tokens run the 32-head token-split stage 1 and shorter ones
+ *                the stage 1 whose waves share each tile (two launches, each
+ *                skipping the other's requests).  The choice depends on the
+ *                request's own length only, so a request still decodes to the
+ *                same bits in any batch that uses the same split_len.  It pays
+ *                when the batch's requests are too few to fill the GPU with
+ *                shared-tile workgroups and costs when they are many (each
+ *                token-split workgroup of 32 heads reads every tile of its
+ *                request; the shared-tile one reads it once for up to 128
+ *                heads), which a batch-invariant rule cannot see, so it is the
+ *                caller's choice.  0 or negative = off (the default).
+ *   reserved   : must be zero.
  */
 typedef struct {
   int partition;
@@ -306,7 +322,8 @@ typedef struct {
   int grid;
   int heads_per_group;
   void* stage_events[3];
-  int reserved[4];
+  int split_len;
+  int reserved[3];
 } mla_decode_opts_t;
 
 /* mla_decode with explicit controls (opts may be NULL = all defaults).

@@ -33,7 +33,7 @@ class MLAError(RuntimeError):
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("partition", ctypes.c_int), ("kernel", ctypes.c_int), ("grid", ctypes.c_int),
                 ("heads_per_group", ctypes.c_int), ("stage_events", ctypes.c_void_p * 3),
-                ("reserved", ctypes.c_int * 4)]
+                ("split_len", ctypes.c_int), ("reserved", ctypes.c_int * 3)]
 
 
 _lib = None
@@ -211,7 +211,7 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
            kv_scale: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
            o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
            partition: int = 0, kernel: int = 0, grid: int = 0, heads_per_group: int = 0,
-           stage_events=None) -> Tuple[torch.Tensor, torch.Tensor]:
+           stage_events=None, split_len: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """MLA decode of q [B, H, R+P] against the paged latent cache.  Returns
     o [B, H, R] (q's dtype) and the natural-log lse [B, H] (fp32).
 
@@ -229,7 +229,8 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
         o_flat = o.view(B, T * H, -1) if o is not None else None
         lse_flat = lse.view(B, T * H) if lse is not None else None
         of, lf = decode(flat, kv_cache, block_table, seq_lens, sm_scale, num_kv_splits, kv_lora_rank, kv_scale,
-                        workspace, o_flat, lse_flat, partition, kernel, grid, heads_per_group, stage_events)
+                        workspace, o_flat, lse_flat, partition, kernel, grid, heads_per_group, stage_events,
+                        split_len)
         return of.view(B, T, H, -1), lf.view(B, T, H)
     B, H, D = q.shape
     R = kv_lora_rank
@@ -260,6 +261,7 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
         raise ValueError("o must be [B, H, R] and lse [B, H]")
     _same_gpu(q, kv_cache, block_table, seq_lens, kv_scale, workspace, o, lse)
     opts = DecodeOpts(partition, kernel, grid, heads_per_group)
+    opts.split_len = split_len
     if stage_events is not None:   # three torch.cuda.Event (or None) recorded around the two stages
         for i, ev in enumerate(stage_events):
             opts.stage_events[i] = ev.cuda_event if ev is not None else None

@@ -1,6 +1,7 @@
 // C ABI of libmla_amd (declared in include/mla.h): argument validation,
 // split planning and kernel launches.  Nothing here reads device memory,
 // allocates, or synchronises, so every call can be captured into a HIP graph.
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -199,7 +200,7 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
   memset(&op, 0, sizeof(op));
   if (opts) op = *opts;
   if (op.partition < 0 || op.partition > 2 || op.kernel < 0 || op.kernel > 3 || op.grid < 0 ||
-      op.heads_per_group < 0)
+      op.heads_per_group < 0 || op.reserved[0] || op.reserved[1] || op.reserved[2])
     return MLA_ERR_ARG;
 
   const bool pair_ok = (q_dtype == MLA_F32 && cache_dtype == MLA_F32) ||
@@ -267,8 +268,8 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
     p.heads_per_group = 4;
     groups = (H + 3) / 4;
   }
-  // 16-head groups: four waves split each token range (kernel 3) instead of
-  // one wave per range.  It sums a range's tiles in another order than the
+  // 16- or 32-head groups: four waves split each token range (kernel 3)
+  // instead of sharing each tile or one wave per range.  It sums a range's tiles in another order than the
   // one-wave kernels, so under the literal partition (whose results must not
   // depend on the batch) it is the default exactly when the head count
   // allows no group wider than 16, whatever the batch size: then every batch
@@ -279,16 +280,31 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
   // (16-19% faster for long ones, 7% slower for the V2-Lite mix), so there
   // it is opt-in.
   p.token_split = 0;
-  if (use_mfma && p.heads_per_group == 16) {
-    if (op.kernel == 3) {
-      if (cache_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
-      p.token_split = 1;
-    } else if (op.kernel == 0 && cache_dtype == MLA_BF16 && !op.grid && p.partition == PART_LITERAL) {
-      p.token_split = H % 32 != 0 ? 1 : 0;
-    }
-  } else if (op.kernel == 3) {
-    return MLA_ERR_UNSUPPORTED;
+  p.len_min = 0;
+  p.len_max = INT_MAX;
+  if (op.kernel == 3) {
+    if (!use_mfma || cache_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+    if (!op.heads_per_group) p.heads_per_group = 16;
+    if ((p.heads_per_group != 16 && p.heads_per_group != 32) || H % p.heads_per_group != 0)
+      return MLA_ERR_UNSUPPORTED;
+    groups = H / p.heads_per_group;
+    p.token_split = 1;
+  } else if (use_mfma && p.heads_per_group == 16 && op.kernel == 0 && cache_dtype == MLA_BF16 && !op.grid &&
+             p.partition == PART_LITERAL) {
+    p.token_split = H % 32 != 0 ? 1 : 0;
   }
+  // Batch-invariant decode (one partial per request) with a head count that
+  // 32 divides, if the caller asks for it: a long request can be served by
+  // four waves that each stream a quarter of its tiles for 32 heads (its
+  // 32-head groups re-read each tile from L2) instead of the fill rule's
+  // shared-tile groups, which leave SIMDs idle when the requests are few.
+  // The two kernels sum a request's tiles in different orders, so the choice
+  // is made per request from its own length (in the kernels: each launch
+  // skips the requests of the other), never from the batch.
+  int split_len = 0;
+  if (use_mfma && op.kernel == 0 && !op.grid && !op.heads_per_group && cache_dtype == MLA_BF16 &&
+      num_kv_splits == 1 && H % 32 == 0 && op.split_len > 0)
+    split_len = op.split_len;
   if (op.grid) {
     p.G = op.grid;
   } else if (p.token_split) {
@@ -313,8 +329,18 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(op.stage_events);
   if (ev[0] && hipEventRecord(ev[0], st) != hipSuccess) return MLA_ERR_HIP;
-  hipError_t e = use_mfma ? launch_stage1_mfma(cache_dtype, kv_lora_rank, p, st)
-                          : launch_stage1_valu(q_dtype, cache_dtype, kv_lora_rank, p, st);
+  hipError_t e;
+  if (split_len > 0) {
+    DecodeParams pt = p;
+    pt.heads_per_group = 32;
+    pt.token_split = 1;
+    pt.len_min = split_len;
+    e = launch_stage1_mfma(cache_dtype, kv_lora_rank, pt, st);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    p.len_max = split_len;
+  }
+  e = use_mfma ? launch_stage1_mfma(cache_dtype, kv_lora_rank, p, st)
+               : launch_stage1_valu(q_dtype, cache_dtype, kv_lora_rank, p, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
   if (ev[1] && hipEventRecord(ev[1], st) != hipSuccess) return MLA_ERR_HIP;
   e = launch_stage2(q_dtype, kv_lora_rank, p, st);

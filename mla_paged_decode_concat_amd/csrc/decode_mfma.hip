@@ -665,42 +665,47 @@ struct Stage1 {
   }
 };
 
-// Token-split stage 1 for one 16-head group (bf16 cache).  When the token
-// ranges are few (the partial-slot cap binds, or the literal partition has
-// fewer items than CUs), a one-wave workgroup per range would leave each busy
-// CU with a single load stream.  Here four waves share the range's 16 heads:
-// wave w streams tiles w, w+4, ... into its own LDS slot (its own 32-token
-// tile, loaded by its own 36 instructions and waited on by itself alone),
-// with its own Q copy, accumulators and online softmax (a head's reference
-// moves up when a tile exceeds it by more than kSlack, rescaling that wave's
-// accumulators, which are few enough here to live in vector registers).  At
-// the end the four partial states are merged through LDS into the range's
-// one partial -- the same quantity the other kernels store.
-template <int R>
+// Token-split stage 1 for one group of 16 * NB heads (bf16 cache).  When
+// the token ranges are few (the partial-slot cap binds, or the literal
+// partition has fewer items than CUs), a workgroup whose waves share each
+// tile would leave each busy CU with a single load stream.  Here four waves
+// share the range's heads: wave w streams tiles w, w+4, ... into its own LDS
+// slot (its own 32-token tile, loaded by its own 36 instructions and waited
+// on by itself alone), with its own Q copy, accumulators and softmax
+// reference (set by its first tile; a later tile more than kSlack above it
+// makes the workgroup redo the range with the larger reference, as in the
+// shared-tile kernel, so the accumulators are never rescaled and stay in
+// the accumulation registers).  At the end the four partial states are
+// merged through LDS, 16 heads at a time, into the range's one partial --
+// the same quantity the other kernels store.
+template <int R, int NB>
 struct Stage1TS {
   using G = Geo<R>;
   using TL = TileLoad<R, 1>;
+  static_assert(NB == 1 || NB == 2, "16 or 32 heads");
   static constexpr int NW_ = 4;
-  static constexpr int HPG = 16;
+  static constexpr int HPG = 16 * NB;
   static constexpr int SLOT = G::TILE_BYTES;
   static constexpr int SMEM = 4 * SLOT;
   static constexpr int TABLE = kTableWindow;
-  static constexpr int MERGE_STAT = 4 * 16 * R;     // floats: per-wave accumulators, then statistics
+  static constexpr int MERGE_STAT = 4 * 16 * R;     // floats: per-wave accumulators of 16 heads, then statistics
   static_assert((MERGE_STAT + 4 * 3 * 16) * 4 <= SMEM, "merge area inside the tile slots");
 
   static __device__ void piece(const DecodeParams& p, int b, int a, int e, int part, int head0,
                                char* smem, int* s_table, int* s_flags) {
-    (void)s_flags;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 4;
     const int r16 = lane & 15;
-    const int h = head0 + r16;
 
-    bf16x8_t qf[G::KS];
-    const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + (long long)b * p.q_sb + (long long)h * p.q_sh;
+    bf16x8_t qf[NB][G::KS];
 #pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qb + 32 * ks + 8 * g);
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint16_t* qb =
+          reinterpret_cast<const uint16_t*>(p.q) + (long long)b * p.q_sb + (long long)(head0 + 16 * nb + r16) * p.q_sh;
+#pragma unroll
+      for (int ks = 0; ks < G::KS; ++ks) qf[nb][ks] = *reinterpret_cast<const bf16x8_t*>(qb + 32 * ks + 8 * g);
+    }
     wait_vmcnt<0>();
 
     uint32_t k_off[2];
@@ -718,15 +723,32 @@ struct Stage1TS {
       v_off[k] = (uint32_t)(tqo * 1024 + (8 * t8 + (c8 ^ TL::swz(t8, tqo))) * 16 + (sg & 1) * 8);
     }
 
-    f32x4_t acc[G::CB];
+    f32x4_t acc[G::CB][NB];
+    float m_ref[NB], l_sum[NB], l_mma[NB], m_init[NB];
 #pragma unroll
-    for (int cb = 0; cb < G::CB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_ref = -INFINITY, l_sum = 0.0f, l_mma = 0.0f;
+    for (int nb = 0; nb < NB; ++nb) m_init[nb] = -INFINITY;
     const float c2 = p.sm_scale * kLog2e;
     const int bs = p.block_size;
     const int32_t* btab = p.block_table + (long long)b * p.bt_stride;
     char* slot = smem + wave * SLOT;
 
+    // One pass over the range per softmax reference; the redo flag of pass
+    // k is s_flags[k & 1] (the other one is cleared for the next pass while
+    // no wave can touch it).
+    if (threadIdx.x == 0) s_flags[0] = 0;
+#pragma unroll 1
+    for (int pass = 0;; ++pass) {
+#pragma unroll
+    for (int cb = 0; cb < G::CB; ++cb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[cb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      m_ref[nb] = m_init[nb];
+      l_sum[nb] = 0.0f;
+      l_mma[nb] = 0.0f;
+    }
+    bool over = false;
     for (int sa = a; sa < e;) {
       const int pg0 = sa / bs;
       const long long win_end = (long long)(pg0 + kTableWindow) * bs;
@@ -744,9 +766,11 @@ struct Stage1TS {
         wait_vmcnt<0>();   // this wave's own tile; no other wave reads it
         const char* tile = slot;
 
-        f32x4_t sc[2];
-        sc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        sc[1] = sc[0];
+        f32x4_t sc[2][NB];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) sc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         bf16x8_t kr[3][2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
@@ -764,45 +788,47 @@ struct Stage1TS {
           }
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
-            sc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks % 3][mb], qf[ks], sc[mb], 0, 0, 0);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+              sc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks % 3][mb], qf[nb][ks], sc[mb][nb], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
 
-        // online softmax in the log2 domain; lane owns head r16, tokens 16mb + 4g + i
-        float mt = -INFINITY;
+        // online softmax in the log2 domain; lane owns head 16nb + r16, tokens 16mb + 4g + i
+        bf16x8_t pf[NB];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int nb = 0; nb < NB; ++nb) {
+          float mt = -INFINITY;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int tok = tile_start + 16 * mb + 4 * g + i;
-            const float v = tok < se ? sc[mb][i] * c2 : -INFINITY;
-            sc[mb][i] = v;
-            mt = fmaxf(mt, v);
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int tok = tile_start + 16 * mb + 4 * g + i;
+              const float v = tok < se ? sc[mb][nb][i] * c2 : -INFINITY;
+              sc[mb][nb][i] = v;
+              mt = fmaxf(mt, v);
+            }
+          if (__builtin_expect(__any(mt > m_ref[nb] + kSlack), 0)) {   // also true while m_ref is unset
+            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+            if (m_ref[nb] == -INFINITY) {
+              m_ref[nb] = mt;                        // this wave's first tile of the pass
+            } else if (mt > m_ref[nb] + kSlack) {
+              m_init[nb] = mt;                       // not representable in this pass
+              over = true;
+            }
           }
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const bool up = mt > m_ref + kSlack;     // also true while m_ref is unset
-        if (__builtin_expect(__any(up), 0)) {
-          if (up) {
-            const float f = __builtin_amdgcn_exp2f(m_ref - mt);   // 0 while unset
 #pragma unroll
-            for (int cb = 0; cb < G::CB; ++cb) acc[cb] *= f;
-            l_sum *= f;
-            l_mma *= f;
-            m_ref = mt;
-          }
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float pj = __builtin_amdgcn_exp2f(sc[mb][nb][i] - m_ref[nb]);
+              const __bf16 pb = (__bf16)pj;
+              l_sum[nb] += pj;
+              l_mma[nb] += (float)pb;
+              pf[nb][4 * mb + i] = pb;
+            }
         }
-        bf16x8_t pf;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pj = __builtin_amdgcn_exp2f(sc[mb][i] - m_ref);
-            const __bf16 pb = (__bf16)pj;
-            l_sum += pj;
-            l_mma += (float)pb;
-            pf[4 * mb + i] = pb;
-          }
 
         auto vread = [&](int cb) -> bf16x8_t {
           const char* vb = tile + (cb >> 2) * 4096 + v_off[cb & 3];
@@ -818,53 +844,66 @@ struct Stage1TS {
 #pragma unroll
         for (int cb = 0; cb < G::CB; ++cb) {
           if (cb + 2 < G::CB) vr[(cb + 2) % 3] = vread(cb + 2);
-          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[cb % 3], pf, acc[cb], 0, 0, 0);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[cb % 3], pf[nb], acc[cb][nb], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
       sa = se;
     }
+    if (over) s_flags[pass & 1] = 1;
+    __syncthreads();   // every wave's flag is in
+    const bool redo = s_flags[pass & 1] != 0;
+    if (threadIdx.x == 0) s_flags[(pass + 1) & 1] = 0;
+    if (!redo) break;
+    }
 
-    // ---- merge the four waves' states into the range's partial
-    l_sum += __shfl_xor(l_sum, 16, 64);
-    l_sum += __shfl_xor(l_sum, 32, 64);
-    l_mma += __shfl_xor(l_mma, 16, 64);
-    l_mma += __shfl_xor(l_mma, 32, 64);
-    __syncthreads();   // every wave is done with its tile slot
+    // ---- merge the four waves' states into the range's partial, 16 heads at a time
     float* mrg = reinterpret_cast<float*>(smem);
     float* stat = mrg + MERGE_STAT;
 #pragma unroll
-    for (int cb = 0; cb < G::CB; ++cb)
-      *MLA_LDS(f32x4_t, mrg + ((wave * G::CB + cb) * 64 + lane) * 4) = acc[cb];
-    if (g == 0) {
-      stat[(wave * 3 + 0) * 16 + r16] = m_ref;
-      stat[(wave * 3 + 1) * 16 + r16] = l_sum;
-      stat[(wave * 3 + 2) * 16 + r16] = l_mma;
+    for (int nb = 0; nb < NB; ++nb) {
+      float ls = l_sum[nb], lm = l_mma[nb];
+      ls += __shfl_xor(ls, 16, 64);
+      ls += __shfl_xor(ls, 32, 64);
+      lm += __shfl_xor(lm, 16, 64);
+      lm += __shfl_xor(lm, 32, 64);
+      __syncthreads();   // every wave is done with its tile slot (or with the previous 16 heads' merge)
+#pragma unroll
+      for (int cb = 0; cb < G::CB; ++cb)
+        *MLA_LDS(f32x4_t, mrg + ((wave * G::CB + cb) * 64 + lane) * 4) = acc[cb][nb];
+      if (g == 0) {
+        stat[(wave * 3 + 0) * 16 + r16] = m_ref[nb];
+        stat[(wave * 3 + 1) * 16 + r16] = ls;
+        stat[(wave * 3 + 2) * 16 + r16] = lm;
+      }
+      __syncthreads();
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, stat[(w * 3) * 16 + r16]);
+      float wt[4], Ls = 0.0f, Lm = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mw = stat[(w * 3) * 16 + r16];
+        wt[w] = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);   // a wave without tiles adds nothing
+        Ls += wt[w] * stat[(w * 3 + 1) * 16 + r16];
+        Lm += wt[w] * stat[(w * 3 + 2) * 16 + r16];
+      }
+      const float inv = 1.0f / Lm;
+      const int h = head0 + 16 * nb + r16;
+      float* dst = ws_row(p, part, h, R);
+      constexpr int CPW = G::CB / 4;   // column blocks each wave writes
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) {
+        const int cb = wave * CPW + j;
+        f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) o += wt[w] * *MLA_LDS(const f32x4_t, mrg + ((w * G::CB + cb) * 64 + lane) * 4);
+        *reinterpret_cast<f32x4_t*>(dst + 16 * cb + 4 * g) = o * inv;
+      }
+      if (wave == 0 && g == 0) *ws_lse(p, part, h, R) = (M + __builtin_amdgcn_logf(Ls)) * kLn2;
     }
-    __syncthreads();
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, stat[(w * 3) * 16 + r16]);
-    float wt[4], Ls = 0.0f, Lm = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = stat[(w * 3) * 16 + r16];
-      wt[w] = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);   // a wave without tiles adds nothing
-      Ls += wt[w] * stat[(w * 3 + 1) * 16 + r16];
-      Lm += wt[w] * stat[(w * 3 + 2) * 16 + r16];
-    }
-    const float inv = 1.0f / Lm;
-    float* dst = ws_row(p, part, h, R);
-    constexpr int CPW = G::CB / 4;   // column blocks each wave writes
-#pragma unroll
-    for (int j = 0; j < CPW; ++j) {
-      const int cb = wave * CPW + j;
-      f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) o += wt[w] * *MLA_LDS(const f32x4_t, mrg + ((w * G::CB + cb) * 64 + lane) * 4);
-      *reinterpret_cast<f32x4_t*>(dst + 16 * cb + 4 * g) = o * inv;
-    }
-    if (wave == 0 && g == 0) *ws_lse(p, part, h, R) = (M + __builtin_amdgcn_logf(Ls)) * kLn2;
     __syncthreads();   // the merge area is tile slots again for the next piece
   }
 };
@@ -928,7 +967,7 @@ __global__ __launch_bounds__(K::NW_ * 64) void stage1_mfma_kernel(DecodeParams p
       const int kps = (n + p.S - 1) / p.S;
       a = s * kps;
       e = min(a + kps, n);
-      if (n <= 0 || e <= a) break;
+      if (n <= 0 || e <= a || n < p.len_min || n >= p.len_max) break;
     } else {
       while (mask == 0) {
         if (base >= 0) carry += __shfl(incl, kWave - 1, kWave);
@@ -1036,10 +1075,13 @@ static hipError_t launch_r(const DecodeParams& p, hipStream_t stream) {
   switch (p.heads_per_group) {
     case 128: return launch_k<Stage1<R, 2, 4, stages_for<R, 4, F8>(), F8>>(p, stream);
     case 64: return launch_k<Stage1<R, 2, 2, stages_for<R, 2, F8>(), F8>>(p, stream);
-    case 32: return launch_k<Stage1<R, 2, 1, stages_for<R, 1, F8>(), F8>>(p, stream);
+    case 32:
+      if constexpr (!F8)
+        if (p.token_split) return launch_k<Stage1TS<R, 2>>(p, stream);
+      return launch_k<Stage1<R, 2, 1, stages_for<R, 1, F8>(), F8>>(p, stream);
     case 16:
       if constexpr (!F8)
-        if (p.token_split) return launch_k<Stage1TS<R>>(p, stream);
+        if (p.token_split) return launch_k<Stage1TS<R, 1>>(p, stream);
       return launch_k<Stage1<R, 1, 1, stages_for<R, 1, F8>(), F8>>(p, stream);
     default: return hipErrorInvalidValue;
   }

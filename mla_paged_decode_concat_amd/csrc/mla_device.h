@@ -206,7 +206,9 @@ struct DecodeParams {
   int partition;                   // PART_LITERAL | PART_BALANCED
   int G;                           // balanced: chunk count
   int heads_per_group;             // stage 1: heads per workgroup
-  int token_split;                 // stage 1, 16-head groups: four waves split the tokens
+  int token_split;                 // stage 1, 16- or 32-head groups: four waves split the tokens
+  int len_min, len_max;            // literal partition: this stage-1 launch takes the requests
+                                   // with len_min <= seq_len < len_max
 };
 
 // Workspace layout (fp32, B*H*S*(R+1) values as the split workspace of the

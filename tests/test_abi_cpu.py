@@ -124,6 +124,12 @@ def test_decode_ex_validation():
     assert _decode(O_(0, 0, -1, 0)) == -1
     assert _decode(O_(0, 2, 0, 0), q_dt=0, cache_dt=0) == -2   # MFMA kernel needs a bf16 query
     assert _decode(O_(0, 0, 0, 0), B=0) == 0
+    bad = O_(0, 0, 0, 0)
+    bad.reserved[1] = 7
+    assert _decode(bad) == -1                                  # reserved fields must be zero
+    assert _decode(O_(0, 3, 0, 64)) == -2                      # token split takes 16- or 32-head groups
+    assert _decode(O_(0, 3, 0, 32), H=48) == -1                # a head group must divide the head count
+    assert _decode(O_(0, 3, 0, 16), cache_dt=2, kvs=FAKE) == -2   # ... of a bf16 cache
 
 
 def _merge(**kw):

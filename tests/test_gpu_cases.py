@@ -109,7 +109,7 @@ def test_late_dominant_token_forces_redo():
     _write(bt)
     o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
     assert np.all(lse_ref > 150)
-    for hpg, kernel in [(32, 2), (128, 2), (16, 3)]:
+    for hpg, kernel in [(32, 2), (128, 2), (16, 3), (32, 3)]:
         for S in [1, 4]:
             _print(f"[redo] hpg={hpg} kernel={kernel} S={S}")
             o, lse = _decode(bt, S, kernel=kernel, heads_per_group=hpg)
@@ -307,11 +307,12 @@ def test_single_split_result_independent_of_head_grouping():
 
 
 
+@pytest.mark.parametrize("hpg", [16, 32])
 @pytest.mark.parametrize("index", [1, 3])
-def test_token_split_kernel(index):
-    """Four waves splitting each token range of a 16-head group (kernel 3):
-    ragged, empty, one-token and long requests, both partitions, several
-    split counts, two head groups, against the oracle."""
+def test_token_split_kernel(index, hpg):
+    """Four waves splitting each token range of a 16- or 32-head group
+    (kernel 3): ragged, empty, one-token and long requests, both partitions,
+    several split counts, one or two head groups, against the oracle."""
     lens = [0, 1, 31, 33, 700, 2500, 129, 5000]
     bt = W.make_batch(index, DEV, seq_lens=lens, H=32)    # block 64 (R=512) and block 16 (R=256)
     ref_cache = oracle_cache(bt)
@@ -319,8 +320,8 @@ def test_token_split_kernel(index):
     o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
     for S in [1, 3, 9]:
         for partition in [1, 2]:
-            _print(f"[ts] workload {index} S={S} partition={partition}")
-            o, lse = _decode(bt, S, kernel=3, heads_per_group=16, partition=partition)
+            _print(f"[ts] workload {index} hpg={hpg} S={S} partition={partition}")
+            o, lse = _decode(bt, S, kernel=3, heads_per_group=hpg, partition=partition)
             compare(o, lse, o_ref, lse_ref, "bf16")
 
 
@@ -328,6 +329,35 @@ def test_token_split_rejects_what_it_cannot_run():
     bt = W.make_batch(4, DEV, B=2, max_len=300, H=16)     # fp8 cache
     with pytest.raises(M.MLAError):
         M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, SM, 2, 512, kv_scale=bt.scale, kernel=3)
-    bt = W.make_batch(1, DEV, B=2, max_len=300, H=32)
+    bt = W.make_batch(1, DEV, B=2, max_len=300, H=64)
+    with pytest.raises(M.MLAError):
+        M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, SM, 2, 512, kernel=3, heads_per_group=64)
+    bt = W.make_batch(1, DEV, B=2, max_len=300, H=48)
     with pytest.raises(M.MLAError):
         M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, SM, 2, 512, kernel=3, heads_per_group=32)
+
+
+@pytest.mark.parametrize("split_len", [4096, 600])
+def test_single_split_length_classes(split_len):
+    """num_kv_splits = 1 with 128 heads and a length threshold: requests of
+    at least split_len tokens take the 32-head token-split kernel and the
+    others the shared-tile kernel, in two launches over the same batch.
+    Results match the oracle, and a request decodes to the same bits alone
+    and inside the batch, on both sides of the threshold."""
+    lens = [4500, 599, 600, 1, 0, 4096, 4095, 1300]
+    bt = W.make_batch(2, DEV, seq_lens=lens, seed=21)
+    ref_cache = oracle_cache(bt)
+    _write(bt)
+    o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
+    o, lse = _decode(bt, 1, split_len=split_len)
+    compare(o, lse, o_ref, lse_ref, "bf16")
+    for b in range(len(lens)):
+        o1, l1 = M.decode(bt.q[b:b + 1].contiguous(), bt.cache, bt.block_table[b:b + 1].contiguous(),
+                          bt.seq_lens[b:b + 1].contiguous(), SM, 1, 512, split_len=split_len)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0], o[b]) and torch.equal(l1[0], lse[b]), b
+    # without a threshold every request takes the shared-tile kernel, which
+    # differs from the token-split one only in rounding
+    o2, l2 = _decode(bt, 1)
+    compare(o2, l2, o_ref, lse_ref, "bf16")
+    assert torch.equal(o2[1], o[1]) and torch.equal(l2[1], lse[1])   # 599 tokens: shared-tile either way
