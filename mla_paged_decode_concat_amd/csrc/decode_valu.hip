@@ -211,19 +211,30 @@ __global__ __launch_bounds__(kWave * kMergeWaves) void stage2_merge_kernel(Decod
   const int hblocks = (p.H + kMergeWaves - 1) / kMergeWaves;
   const int b = blockIdx.x / hblocks;
   const int h = (blockIdx.x - b * hblocks) * kMergeWaves + wave;
-  if (h >= p.H) return;
-  const int n = p.seq_lens[b];
   int k, first;
   if (p.partition == PART_LITERAL) {
-    k = literal_num_partials(n, p.S);
+    k = literal_num_partials(p.seq_lens[b], p.S);
     first = b * p.S;
   } else {
-    long long start;
-    const BatchTotals t = batch_totals_and_start(p.seq_lens, p.B, b, lane, start);
-    const long long Q = balanced_chunk(t, p.G);
-    k = balanced_num_partials(start, n, Q);
-    first = (int)(start / Q) + b;
+    // The workgroup's waves are heads of one request: wave 0 works out the
+    // request's partials for all of them.  (With eight waves per SIMD this
+    // vector work, done by every wave, cost about as much as loading the
+    // partial rows.)
+    __shared__ int s_part[2];
+    if (wave == 0) {
+      long long start;
+      const BatchTotals t = batch_totals_and_start(p.seq_lens, p.B, b, lane, start);
+      const long long Q = balanced_chunk(t, p.G);
+      if (lane == 0) {
+        s_part[0] = balanced_num_partials(start, p.seq_lens[b], Q);
+        s_part[1] = (int)div_nonneg(start, Q) + b;
+      }
+    }
+    __syncthreads();
+    k = s_part[0];
+    first = s_part[1];
   }
+  if (h >= p.H) return;
   k = __builtin_amdgcn_readfirstlane(k);
   first = __builtin_amdgcn_readfirstlane(first);
   // the request's partials are consecutive slots: partial s at rows + s R / 4
