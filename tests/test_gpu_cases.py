@@ -337,15 +337,17 @@ def test_token_split_rejects_what_it_cannot_run():
         M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, SM, 2, 512, kernel=3, heads_per_group=32)
 
 
-@pytest.mark.parametrize("split_len", [4096, 600])
-def test_single_split_length_classes(split_len):
-    """num_kv_splits = 1 with 128 heads and a length threshold: requests of
-    at least split_len tokens take the 32-head token-split kernel and the
-    others the shared-tile kernel, in two launches over the same batch.
-    Results match the oracle, and a request decodes to the same bits alone
-    and inside the batch, on both sides of the threshold."""
+@pytest.mark.parametrize("index,split_len", [(2, 4096), (2, 600), (3, 600)])
+def test_single_split_length_classes(index, split_len):
+    """num_kv_splits = 1 with a length threshold (128 heads of 576-wide
+    rows, 32 heads of 320-wide rows): requests of at least split_len tokens
+    take the 32-head token-split kernel and the others the shared-tile
+    kernel, in two launches over the same batch.  Results match the oracle,
+    and a request decodes to the same bits alone and inside the batch, on
+    both sides of the threshold."""
     lens = [4500, 599, 600, 1, 0, 4096, 4095, 1300]
-    bt = W.make_batch(2, DEV, seq_lens=lens, seed=21)
+    bt = W.make_batch(index, DEV, seq_lens=lens, seed=21)
+    R = bt.spec.R
     ref_cache = oracle_cache(bt)
     _write(bt)
     o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
@@ -353,7 +355,7 @@ def test_single_split_length_classes(split_len):
     compare(o, lse, o_ref, lse_ref, "bf16")
     for b in range(len(lens)):
         o1, l1 = M.decode(bt.q[b:b + 1].contiguous(), bt.cache, bt.block_table[b:b + 1].contiguous(),
-                          bt.seq_lens[b:b + 1].contiguous(), SM, 1, 512, split_len=split_len)
+                          bt.seq_lens[b:b + 1].contiguous(), SM, 1, R, split_len=split_len)
         torch.cuda.synchronize()
         assert torch.equal(o1[0], o[b]) and torch.equal(l1[0], lse[b]), b
     # without a threshold every request takes the shared-tile kernel, which
