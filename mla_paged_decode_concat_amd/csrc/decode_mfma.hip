@@ -94,12 +94,26 @@ __device__ __forceinline__ void wait_vmcnt() {
 // every later LDS read (it cannot prove the in-flight tile and the tile being
 // read are disjoint); the kernel orders them itself with wait_vmcnt + a
 // workgroup barrier.
+//
+// nt (wave-uniform) sets the load's non-temporal hint: the lines are not
+// expected to be read again, so they do not displace reusable data in L2
+// and the last-level cache.  That holds when one workgroup reads each tile
+// (a single head group); tiles shared by several head groups meet in L2
+// and are loaded without it.  Measured on the V3 shape (128 heads, one
+// group): stage 1 172 -> 161 us, and stage 2, which reads the partials that
+// stage 1 leaves in the caches, 17.7 -> 17.0 us.
 template <int OFF>
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base, bool nt) {
   static_assert(OFF >= 0 && OFF < 4096, "immediate offset");
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2" ::"v"(gptr),
-               "s"(__builtin_amdgcn_readfirstlane(lds_base - OFF)), "i"(OFF)
-               : "memory");
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base - OFF);
+  if (nt)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2 nt" ::"v"(gptr), "s"(m0),
+                 "i"(OFF)
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2" ::"v"(gptr), "s"(m0),
+                 "i"(OFF)
+                 : "memory");
 }
 
 // This lane's index, read so that the compiler cannot hoist what is derived
@@ -160,6 +174,7 @@ struct TileLoad {
 
   struct Rows {
     const char* r[NQ];
+    bool nt;                                       // non-temporal hint on the loads
   };
   static __device__ __forceinline__ Rows rows(const DecodeParams& p, int tile_start, int se, int pg0,
                                               const int* s_table, int wave) {
@@ -167,6 +182,7 @@ struct TileLoad {
     const int lane = lane_now();
     const int t8 = lane >> 3, x = lane & 7;
     Rows rw;
+    rw.nt = __builtin_amdgcn_readfirstlane(p.kv_nt) != 0;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       const int tq = wave + NW * j;
@@ -185,9 +201,9 @@ struct TileLoad {
   static __device__ __forceinline__ void issue(const Rows& rw, const char* vbuf, const char* rbuf, int wave) {
     constexpr int j = I % NQ, cq8 = I / NQ;
     if constexpr (cq8 < CQ - 1)
-      dma16<128 * cq8>(rw.r[j], lds_addr(vbuf) + (wave + NW * j + 4 * cq8) * 1024);
+      dma16<128 * cq8>(rw.r[j], lds_addr(vbuf) + (wave + NW * j + 4 * cq8) * 1024, rw.nt);
     else
-      dma16<128 * cq8>(rw.r[j], lds_addr(rbuf) + (wave + NW * j) * 1024);
+      dma16<128 * cq8>(rw.r[j], lds_addr(rbuf) + (wave + NW * j) * 1024, rw.nt);
   }
   static __device__ __forceinline__ void tile(const DecodeParams& p, int tile_start, int se, int pg0,
                                               const char* vbuf, const char* rbuf, const int* s_table, int wave,
@@ -222,6 +238,7 @@ struct TileLoad8 {
   struct Rows {
     const char* full[NQ];
     const char* rope[NQ];
+    bool nt;                                       // non-temporal hint on the loads
   };
   static __device__ __forceinline__ const char* row_ptr(const DecodeParams& p, int tok, int se, int pg0,
                                                         const int* s_table) {
@@ -234,6 +251,7 @@ struct TileLoad8 {
                                               const int* s_table, int wave) {
     const int lane = lane_now();
     Rows rw;
+    rw.nt = __builtin_amdgcn_readfirstlane(p.kv_nt) != 0;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       const int tq = wave + NW * j;
@@ -250,9 +268,9 @@ struct TileLoad8 {
     constexpr int j = I / (FG + 1), k = I % (FG + 1);
     const int tq = wave + NW * j;
     if constexpr (k < FG) {
-      dma16<128 * k>(rw.full[j], lds_addr(buf) + (4 * k + tq) * 1024);
+      dma16<128 * k>(rw.full[j], lds_addr(buf) + (4 * k + tq) * 1024, rw.nt);
     } else {
-      if (lane < 32) dma16<0>(rw.rope[j], lds_addr(buf) + ROPE_OFF + tq * 512);
+      if (lane < 32) dma16<0>(rw.rope[j], lds_addr(buf) + ROPE_OFF + tq * 512, rw.nt);
     }
   }
   static __device__ __forceinline__ void tile(const DecodeParams& p, int tile_start, int se, int pg0,
