@@ -95,18 +95,19 @@ __device__ __forceinline__ void wait_vmcnt() {
 // read are disjoint); the kernel orders them itself with wait_vmcnt + a
 // workgroup barrier.
 //
-// nt (wave-uniform) sets the load's non-temporal hint: the lines are not
+// NT sets the load's non-temporal hint (a compile-time choice: a branch
+// around every load instruction slowed the one-wave kernels by half): the lines are not
 // expected to be read again, so they do not displace reusable data in L2
 // and the last-level cache.  That holds when one workgroup reads each tile
 // (a single head group); tiles shared by several head groups meet in L2
 // and are loaded without it.  Measured on the V3 shape (128 heads, one
 // group): stage 1 172 -> 161 us, and stage 2, which reads the partials that
 // stage 1 leaves in the caches, 17.7 -> 17.0 us.
-template <int OFF>
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base, bool nt) {
+template <int OFF, bool NT>
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
   static_assert(OFF >= 0 && OFF < 4096, "immediate offset");
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base - OFF);
-  if (nt)
+  if constexpr (NT)
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2 nt" ::"v"(gptr), "s"(m0),
                  "i"(OFF)
                  : "memory");
@@ -174,7 +175,6 @@ struct TileLoad {
 
   struct Rows {
     const char* r[NQ];
-    bool nt;                                       // non-temporal hint on the loads
   };
   static __device__ __forceinline__ Rows rows(const DecodeParams& p, int tile_start, int se, int pg0,
                                               const int* s_table, int wave) {
@@ -182,7 +182,6 @@ struct TileLoad {
     const int lane = lane_now();
     const int t8 = lane >> 3, x = lane & 7;
     Rows rw;
-    rw.nt = __builtin_amdgcn_readfirstlane(p.kv_nt) != 0;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       const int tq = wave + NW * j;
@@ -197,19 +196,20 @@ struct TileLoad {
   }
   // a tile's column groups cq8 < CQ-1 (values) go to vbuf, the last (rope) to rbuf
   static constexpr int CQ = G::CHUNKS / 8;
-  template <int I>
+  template <int I, bool NT>
   static __device__ __forceinline__ void issue(const Rows& rw, const char* vbuf, const char* rbuf, int wave) {
     constexpr int j = I % NQ, cq8 = I / NQ;
     if constexpr (cq8 < CQ - 1)
-      dma16<128 * cq8>(rw.r[j], lds_addr(vbuf) + (wave + NW * j + 4 * cq8) * 1024, rw.nt);
+      dma16<128 * cq8, NT>(rw.r[j], lds_addr(vbuf) + (wave + NW * j + 4 * cq8) * 1024);
     else
-      dma16<128 * cq8>(rw.r[j], lds_addr(rbuf) + (wave + NW * j) * 1024, rw.nt);
+      dma16<128 * cq8, NT>(rw.r[j], lds_addr(rbuf) + (wave + NW * j) * 1024);
   }
+  template <bool NT>
   static __device__ __forceinline__ void tile(const DecodeParams& p, int tile_start, int se, int pg0,
                                               const char* vbuf, const char* rbuf, const int* s_table, int wave,
                                               int lane) {
     const Rows rw = rows(p, tile_start, se, pg0, s_table, wave);
-    static_for<LPW>([&](auto i) { issue<decltype(i)::value>(rw, vbuf, rbuf, wave); });
+    static_for<LPW>([&](auto i) { issue<decltype(i)::value, NT>(rw, vbuf, rbuf, wave); });
   }
 };
 
@@ -238,7 +238,6 @@ struct TileLoad8 {
   struct Rows {
     const char* full[NQ];
     const char* rope[NQ];
-    bool nt;                                       // non-temporal hint on the loads
   };
   static __device__ __forceinline__ const char* row_ptr(const DecodeParams& p, int tok, int se, int pg0,
                                                         const int* s_table) {
@@ -251,7 +250,6 @@ struct TileLoad8 {
                                               const int* s_table, int wave) {
     const int lane = lane_now();
     Rows rw;
-    rw.nt = __builtin_amdgcn_readfirstlane(p.kv_nt) != 0;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       const int tq = wave + NW * j;
@@ -263,20 +261,21 @@ struct TileLoad8 {
     }
     return rw;
   }
-  template <int I>
+  template <int I, bool NT>
   static __device__ __forceinline__ void issue(const Rows& rw, const char* buf, int wave, int lane) {
     constexpr int j = I / (FG + 1), k = I % (FG + 1);
     const int tq = wave + NW * j;
     if constexpr (k < FG) {
-      dma16<128 * k>(rw.full[j], lds_addr(buf) + (4 * k + tq) * 1024, rw.nt);
+      dma16<128 * k, NT>(rw.full[j], lds_addr(buf) + (4 * k + tq) * 1024);
     } else {
-      if (lane < 32) dma16<0>(rw.rope[j], lds_addr(buf) + ROPE_OFF + tq * 512, rw.nt);
+      if (lane < 32) dma16<0, NT>(rw.rope[j], lds_addr(buf) + ROPE_OFF + tq * 512);
     }
   }
+  template <bool NT>
   static __device__ __forceinline__ void tile(const DecodeParams& p, int tile_start, int se, int pg0,
                                               const char* buf, const int* s_table, int wave, int lane) {
     const Rows rw = rows(p, tile_start, se, pg0, s_table, wave);
-    static_for<LPW>([&](auto i) { issue<decltype(i)::value>(rw, buf, wave, lane); });
+    static_for<LPW>([&](auto i) { issue<decltype(i)::value, NT>(rw, buf, wave, lane); });
   }
 
 };
@@ -318,19 +317,23 @@ struct Stage1 {
   static constexpr bool kStagger = !F8 && NW == 4;
   static constexpr int kIssueAt[4] = {100 + G::KS * 2 / 9, 100 + G::KS * 13 / 18, 300 + G::CB / 4,
                                       300 + G::CB * 3 / 4};
-  template <int I>
+  template <int I, bool NT>
   static __device__ __forceinline__ void issue_part(const typename TileLoad<R, NW>::Rows& rw, char* buf, int wave) {
-    TileLoad<R, NW>::template issue<I>(rw, buf, buf + (G::CHUNKS / 8 - 1) * 4096, wave);
+    TileLoad<R, NW>::template issue<I, NT>(rw, buf, buf + (G::CHUNKS / 8 - 1) * 4096, wave);
   }
+  template <bool NT>
   static __device__ __forceinline__ void issue_tile(const DecodeParams& p, int tile_start, int se, int pg0,
                                                     char* buf, const int* s_table, int wave, int lane) {
     if constexpr (F8)
-      TL8::tile(p, tile_start, se, pg0, buf, s_table, wave, lane);
+      TL8::template tile<NT>(p, tile_start, se, pg0, buf, s_table, wave, lane);
     else
-      TileLoad<R, NW>::tile(p, tile_start, se, pg0, buf, buf + (G::CHUNKS / 8 - 1) * 4096, s_table, wave, lane);
+      TileLoad<R, NW>::template tile<NT>(p, tile_start, se, pg0, buf, buf + (G::CHUNKS / 8 - 1) * 4096, s_table, wave,
+                                         lane);
   }
 
-  // Token range [a, e) of request b for this wave's heads; writes partial slot `part`.
+  // Token range [a, e) of request b for this wave's heads; writes partial
+  // slot `part`.  NT: the tile loads carry the non-temporal hint.
+  template <bool NT>
   static __device__ void piece(const DecodeParams& p, int b, int a, int e, int part, int head0,
                                char* smem, int* s_table, int* s_flags) {
     const int lane = threadIdx.x & 63;
@@ -434,7 +437,7 @@ struct Stage1 {
         const int ntiles = (se - sa + kTile - 1) / kTile;
 #pragma unroll
         for (int t = 0; t < STAGES - 1; ++t)
-          if (t < ntiles) issue_tile(p, sa + kTile * t, se, pg0, smem + t * SLOT, s_table, wave, lane);
+          if (t < ntiles) issue_tile<NT>(p, sa + kTile * t, se, pg0, smem + t * SLOT, s_table, wave, lane);
 
 #pragma unroll 1
         for (int t = 0; t < ntiles; ++t) {
@@ -454,11 +457,11 @@ struct Stage1 {
           char* nbuf = smem + ((t + STAGES - 1) % STAGES) * SLOT;
           typename TileLoad<R, NW>::Rows nrw;
           if constexpr (F8) {
-            if (more) issue_tile(p, sa + kTile * (t + STAGES - 1), se, pg0, nbuf, s_table, wave, lane);
+            if (more) issue_tile<NT>(p, sa + kTile * (t + STAGES - 1), se, pg0, nbuf, s_table, wave, lane);
           } else if constexpr (!kStagger) {
             if (more) {
               nrw = TileLoad<R, NW>::rows(p, sa + kTile * (t + STAGES - 1), se, pg0, s_table, wave);
-              static_for<kFirst>([&](auto i) { issue_part<decltype(i)::value>(nrw, nbuf, wave); });
+              static_for<kFirst>([&](auto i) { issue_part<decltype(i)::value, NT>(nrw, nbuf, wave); });
             }
           }
           // the staggered issue: called at every point, issues in the wave whose point it is
@@ -471,7 +474,7 @@ struct Stage1 {
                 if (more && ((wmask >> wave) & 1)) {
                   const typename TileLoad<R, NW>::Rows rw =
                       TileLoad<R, NW>::rows(p, sa + kTile * (t + STAGES - 1), se, pg0, s_table, wave);
-                  static_for<LPW>([&](auto i) { issue_part<decltype(i)::value>(rw, nbuf, wave); });
+                  static_for<LPW>([&](auto i) { issue_part<decltype(i)::value, NT>(rw, nbuf, wave); });
                 }
               }
             }
@@ -551,7 +554,8 @@ struct Stage1 {
           }
 
           if constexpr (!F8 && !kStagger) {
-            if (more) static_for<LPW - kFirst>([&](auto i) { issue_part<kFirst + decltype(i)::value>(nrw, nbuf, wave); });
+            if (more)
+              static_for<LPW - kFirst>([&](auto i) { issue_part<kFirst + decltype(i)::value, NT>(nrw, nbuf, wave); });
           }
           // ---- softmax in the log2 domain; lane owns head r16, tokens 16mb + 4g + i
           bool need = false;
@@ -709,6 +713,7 @@ struct Stage1TS {
   static constexpr int MERGE_STAT = 4 * 16 * R;     // floats: per-wave accumulators of 16 heads, then statistics
   static_assert((MERGE_STAT + 4 * 3 * 16) * 4 <= SMEM, "merge area inside the tile slots");
 
+  template <bool NT>
   static __device__ void piece(const DecodeParams& p, int b, int a, int e, int part, int head0,
                                char* smem, int* s_table, int* s_flags) {
     const int lane = threadIdx.x & 63;
@@ -780,7 +785,7 @@ struct Stage1TS {
 #pragma unroll 1
       for (int t = wave; t < ntiles; t += 4) {
         const int tile_start = sa + kTile * t;
-        TL::tile(p, tile_start, se, pg0, slot, slot + (G::CHUNKS / 8 - 1) * 4096, s_table, 0, lane);
+        TL::template tile<NT>(p, tile_start, se, pg0, slot, slot + (G::CHUNKS / 8 - 1) * 4096, s_table, 0, lane);
         wait_vmcnt<0>();   // this wave's own tile; no other wave reads it
         const char* tile = slot;
 
@@ -944,7 +949,7 @@ __host__ __device__ inline int mapped_grid(int items, int groups) {
   return ((items + kXcds - 1) / kXcds) * kXcds * groups;
 }
 
-template <class K>
+template <class K, bool NT>
 __global__ __launch_bounds__(K::NW_ * 64) void stage1_mfma_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[K::SMEM];
   __shared__ int s_table[K::TABLE];
@@ -1010,7 +1015,7 @@ __global__ __launch_bounds__(K::NW_ * 64) void stage1_mfma_kernel(DecodeParams p
     }
     // the piece is the same for every lane: say so, so that its bounds and
     // loop counters live in scalar registers
-    K::piece(p, __builtin_amdgcn_readfirstlane(b), __builtin_amdgcn_readfirstlane(a),
+    K::template piece<NT>(p, __builtin_amdgcn_readfirstlane(b), __builtin_amdgcn_readfirstlane(a),
              __builtin_amdgcn_readfirstlane(e), __builtin_amdgcn_readfirstlane(part),
              __builtin_amdgcn_readfirstlane(head0), smem, s_table, s_flags);
   }
@@ -1084,7 +1089,10 @@ static hipError_t launch_k(const DecodeParams& p, hipStream_t stream) {
   const int groups = (p.H + K::HPG - 1) / K::HPG;
   const int items = p.partition == PART_LITERAL ? p.B * p.S : p.G;
   dim3 grid((unsigned)mapped_grid(items, groups)), block(K::NW_ * 64);
-  hipLaunchKernelGGL((stage1_mfma_kernel<K>), grid, block, 0, stream, p);
+  if (p.kv_nt)
+    hipLaunchKernelGGL((stage1_mfma_kernel<K, true>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((stage1_mfma_kernel<K, false>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
