@@ -329,16 +329,17 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(op.stage_events);
   if (ev[0] && hipEventRecord(ev[0], st) != hipSuccess) return MLA_ERR_HIP;
-  // KV tiles that one workgroup alone reads (all heads in one group) are
-  // streamed past the caches; tiles shared by several head groups are meant
-  // to meet in L2
-  p.kv_nt = groups == 1 ? 1 : 0;
+  // KV tiles read by one or two head groups are streamed past the caches
+  // (the second group's workgroup runs right after the first on the same
+  // XCD and still finds the lines); tiles shared by more groups are meant to
+  // meet in L2
+  p.kv_nt = groups <= 2 ? 1 : 0;
   hipError_t e;
   if (split_len > 0) {
     DecodeParams pt = p;
     pt.heads_per_group = 32;
     pt.token_split = 1;
-    pt.kv_nt = H == 32 ? 1 : 0;
+    pt.kv_nt = H <= 64 ? 1 : 0;
     pt.len_min = split_len;
     e = launch_stage1_mfma(cache_dtype, kv_lora_rank, pt, st);
     if (e != hipSuccess) return MLA_ERR_HIP;

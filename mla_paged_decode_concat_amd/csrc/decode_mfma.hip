@@ -34,9 +34,8 @@
 //  * Each CU keeps only about 36-40 KB of loads in flight before a further
 //    load issue stalls the issuing wave, so a workgroup gets about one tile
 //    per HBM round trip.  With four waves, each issues its loads of the tile
-//    three ahead at its own point of the tile (two inside QK, two inside
-//    PV); narrower workgroups issue theirs in two parts, after the tile
-//    barrier and after QK.
+//    three ahead at its own point of PV; narrower workgroups issue theirs in
+//    two parts, after the tile barrier and after QK.
 //  * Workgroups of 16 or 32 heads are one wave with a two-tile ring, several
 //    to a CU (one wave per SIMD), so their stalls and compute overlap.
 //  * The request's block-table slice is staged in LDS, so page lookups are
@@ -98,11 +97,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // NT sets the load's non-temporal hint (a compile-time choice: a branch
 // around every load instruction slowed the one-wave kernels by half): the lines are not
 // expected to be read again, so they do not displace reusable data in L2
-// and the last-level cache.  That holds when one workgroup reads each tile
-// (a single head group); tiles shared by several head groups meet in L2
-// and are loaded without it.  Measured on the V3 shape (128 heads, one
-// group): stage 1 172 -> 161 us, and stage 2, which reads the partials that
-// stage 1 leaves in the caches, 17.7 -> 17.0 us.
+// and the last-level cache.  That holds when one or two head groups read
+// each tile; tiles shared by more groups meet in L2 and are loaded without
+// it.  Measured on the V3 shape (128 heads, one group): stage 1 172 -> 161
+// us, and stage 2, which reads the partials that stage 1 leaves in the
+// caches, 17.7 -> 17.0 us; two query tokens per request (two 128-row
+// groups) 327 -> 316 us.
 template <int OFF, bool NT>
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
   static_assert(OFF >= 0 && OFF < 4096, "immediate offset");
@@ -310,13 +310,15 @@ struct Stage1 {
   // bf16 tiles, one or two waves: load instructions issued before QK; the rest follow QK
   static constexpr int kFirst = (LPW * 5 + 8) / 9;
   // bf16 tiles, four waves: each wave issues all of its loads for the tile
-  // three ahead at its own point of the tile -- waves 0 and 1 at two QK
-  // k-steps, waves 2 and 3 at two PV column blocks -- so that the four
-  // bursts do not queue behind each other at the CU's load unit.  Points are
-  // encoded as 100 + k-step or 300 + column block.
+  // three ahead at its own PV column block (1/16, 5/16, 9/16 and 13/16 of
+  // the way through PV), so that the four bursts do not queue behind each
+  // other at the CU's load unit and none of them stalls QK, whose K reads
+  // are the denser LDS stream.  (Measured against two points in QK and two
+  // in PV: 156.0 vs 161.9 us, faster in 15 of 16 interleaved rounds.)
+  // Points are encoded as 100 + QK k-step or 300 + PV column block.
   static constexpr bool kStagger = !F8 && NW == 4;
-  static constexpr int kIssueAt[4] = {100 + G::KS * 2 / 9, 100 + G::KS * 13 / 18, 300 + G::CB / 4,
-                                      300 + G::CB * 3 / 4};
+  static constexpr int kIssueAt[4] = {300 + G::CB / 16, 300 + G::CB * 5 / 16, 300 + G::CB * 9 / 16,
+                                      300 + G::CB * 13 / 16};
   template <int I, bool NT>
   static __device__ __forceinline__ void issue_part(const typename TileLoad<R, NW>::Rows& rw, char* buf, int wave) {
     TileLoad<R, NW>::template issue<I, NT>(rw, buf, buf + (G::CHUNKS / 8 - 1) * 4096, wave);

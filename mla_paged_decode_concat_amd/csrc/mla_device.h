@@ -215,7 +215,7 @@ struct DecodeParams {
   int G;                           // balanced: chunk count
   int heads_per_group;             // stage 1: heads per workgroup
   int token_split;                 // stage 1, 16- or 32-head groups: four waves split the tokens
-  int kv_nt;                       // stage-1 tile loads carry the non-temporal hint (one head group)
+  int kv_nt;                       // stage-1 tile loads carry the non-temporal hint (<= 2 head groups)
   int len_min, len_max;            // literal partition: this stage-1 launch takes the requests
                                    // with len_min <= seq_len < len_max
 };
