@@ -121,7 +121,7 @@ def test_late_dominant_token_forces_redo():
 def test_block_sizes(bs, index):
     spec = W.SPECS[index]
     lens = [1, 31, 33, 1500, 2049]
-    bt = W.make_batch(index, DEV, seq_lens=lens, H=16)
+    bt = W.make_batch(index, DEV, seq_lens=lens, H=32)
     # rebuild the paging with block size bs over the same token rows
     nblk = [-(-n // bs) for n in lens]
     g = torch.Generator().manual_seed(bs)
@@ -147,11 +147,14 @@ def test_block_sizes(bs, index):
     _write(bt)
     assert np.array_equal(W.bits(bt.cache), ref_cache)
     o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
+    # the token-split kernels (bf16 cache only) with 16- and 32-head groups;
+    # block size 1 stages the table of a 2049-token request in three windows
+    runs = [(1, 0), (2, 0)] + ([(3, 16), (3, 32)] if spec.cache_dtype == "bf16" else [])
     for S in [1, 4]:
-        for kernel in [1, 2]:
+        for kernel, hpg in runs:
             for partition in [1, 2]:
-                _print(f"[bs] bs={bs} S={S} kernel={kernel} partition={partition}")
-                o, lse = _decode(bt, S, kernel=kernel, partition=partition)
+                _print(f"[bs] bs={bs} S={S} kernel={kernel} hpg={hpg} partition={partition}")
+                o, lse = _decode(bt, S, kernel=kernel, heads_per_group=hpg, partition=partition)
                 compare(o, lse, o_ref, lse_ref, "bf16")
 
 
