@@ -50,6 +50,12 @@ __device__ __forceinline__ uint32_t encode_one(float v, float scale) {
 // that every token's loads are in flight at once.
 int write_tokens_per_wave(long long num_tokens) { return num_tokens <= 65536 ? 1 : 4; }
 
+// The rows are streamed: each input row is read once and each cache row
+// written once per call, so the 16-byte loads and stores carry the
+// non-temporal hint and do not push reusable data out of L2 and the
+// last-level cache (bulk write of 524288 bf16 rows: 244.8 -> 231.5 us).
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+
 // Load `len` input elements of a row into the lanes' vectors; lane j takes
 // elements [V (j + 64 i), V (j + 64 i) + V).
 template <int IT, int N>
@@ -59,7 +65,10 @@ __device__ __forceinline__ void load_vecs(const typename InElem<IT>::T* __restri
 #pragma unroll
   for (int k = 0; k < N; ++k) {
     const int i = (lane + kWave * k) * V;
-    if (i < len) v[k] = *reinterpret_cast<const uint4*>(src + i);
+    if (i < len) {
+      const u32x4_nt t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(src + i));
+      v[k] = make_uint4(t[0], t[1], t[2], t[3]);
+    }
   }
 }
 
@@ -75,7 +84,7 @@ __device__ __forceinline__ void store_vecs(void* __restrict__ dst_base, long lon
     if (i >= len) continue;
     if constexpr (CT == IT) {
       T* dst = reinterpret_cast<T*>(dst_base) + dst_off + i;
-      *reinterpret_cast<uint4*>(dst) = v[k];
+      __builtin_nontemporal_store(u32x4_nt{v[k].x, v[k].y, v[k].z, v[k].w}, reinterpret_cast<u32x4_nt*>(dst));
     } else {
       // fp8 output: V codes from V inputs
       const T* e = reinterpret_cast<const T*>(&v[k]);
