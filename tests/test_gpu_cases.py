@@ -340,16 +340,16 @@ def test_token_split_rejects_what_it_cannot_run():
         M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, SM, 2, 512, kernel=3, heads_per_group=32)
 
 
-@pytest.mark.parametrize("index,split_len", [(2, 4096), (2, 600), (3, 600)])
-def test_single_split_length_classes(index, split_len):
-    """num_kv_splits = 1 with a length threshold (128 heads of 576-wide
-    rows, 32 heads of 320-wide rows): requests of at least split_len tokens
-    take the 32-head token-split kernel and the others the shared-tile
-    kernel, in two launches over the same batch.  Results match the oracle,
-    and a request decodes to the same bits alone and inside the batch, on
-    both sides of the threshold."""
+@pytest.mark.parametrize("index,H,split_len", [(2, 128, 4096), (2, 128, 600), (2, 64, 600), (3, 32, 600)])
+def test_single_split_length_classes(index, H, split_len):
+    """num_kv_splits = 1 with a length threshold (128 or 64 heads of
+    576-wide rows, 32 heads of 320-wide rows): requests of at least
+    split_len tokens take the 32-head token-split kernel and the others the
+    shared-tile kernel, in two launches over the same batch.  Results match
+    the oracle, and a request decodes to the same bits alone and inside the
+    batch, on both sides of the threshold."""
     lens = [4500, 599, 600, 1, 0, 4096, 4095, 1300]
-    bt = W.make_batch(index, DEV, seq_lens=lens, seed=21)
+    bt = W.make_batch(index, DEV, seq_lens=lens, seed=21, H=H)
     R = bt.spec.R
     ref_cache = oracle_cache(bt)
     _write(bt)
