@@ -218,7 +218,11 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
     q may also be [B, q_len, H, R+P]: q_len query tokens per request that all
     attend to the request's whole cached sequence (non-causal multi-token
     decode); they run as q_len * H rows of one request, and o and lse come
-    back as [B, q_len, H, R] and [B, q_len, H]."""
+    back as [B, q_len, H, R] and [B, q_len, H].
+
+    partition, kernel, grid, heads_per_group and split_len are the
+    mla_decode_opts_t controls of include/mla.h (0 = library default);
+    stage_events are three events recorded around the two stages."""
     if isinstance(q, tuple):
         q = torch.cat(q, dim=-1)
     if q.dim() == 4:
