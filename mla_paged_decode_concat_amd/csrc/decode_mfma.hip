@@ -590,7 +590,13 @@ struct Stage1 {
               }
             }
           }
-          bf16x8_t pf[NB];
+          // P for the matrix cores in bf16.  An fp8 cache also gets the
+          // rounding remainder p - bf16(p) as a second bf16 operand (pl): the
+          // value columns are then summed against p to ~16 significant bits.
+          // A weight rounded to bf16 alone is off by up to 2^-9 of itself,
+          // which moves o by up to ~2^-9 |v_j - o| per dominant token; with
+          // the wider values an fp8 cache holds that reached the 1e-2 bound.
+          bf16x8_t pf[NB], pl[F8 ? NB : 1];
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             float ls = 0.0f, lm = 0.0f;
@@ -601,8 +607,14 @@ struct Stage1 {
                 const float pj = __builtin_amdgcn_exp2f(s[mb][nb][i] - m_ref[nb]);
                 const __bf16 pb = (__bf16)pj;
                 ls += pj;
-                lm += (float)pb;
                 pf[nb][4 * mb + i] = pb;
+                if constexpr (F8) {
+                  const __bf16 pr = (__bf16)(pj - (float)pb);
+                  pl[nb][4 * mb + i] = pr;
+                  lm += (float)pb + (float)pr;
+                } else {
+                  lm += (float)pb;
+                }
               }
             l_sum[nb] += ls;
             l_mma[nb] += lm;
@@ -653,8 +665,10 @@ struct Stage1 {
               if (cb + 2 < G::CB) vw[(cb + 2) % 3] = vread8(cb + 2);
               const bf16x8_t vf = fp8x8_to_bf16((uint32_t)vw[cb % 3][0], (uint32_t)vw[cb % 3][1]);
 #pragma unroll
-              for (int nb = 0; nb < NB; ++nb)
+              for (int nb = 0; nb < NB; ++nb) {
                 acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[nb], acc[cb][nb], 0, 0, 0);
+                acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[nb], acc[cb][nb], 0, 0, 0);
+              }
               __builtin_amdgcn_sched_barrier(0);
             }
           }

@@ -1,7 +1,14 @@
 """Seeded random decode configurations against the oracle: batch size, head
 count (including counts only the vector kernel takes), lengths (empty, one
 token, ragged, one long request), num_kv_splits, partition and cache type
-drawn per case -- combinations the targeted tests do not enumerate."""
+drawn per case, and, from a second generator, the stage-1 choice (library
+default, the token-split kernel with 16 or 32 heads, or batch-invariant
+length classes) -- combinations the targeted tests do not enumerate.
+MLA_RANDOM_CASES sets the number of cases (100 by default; seeds 42 and 65
+once exceeded the bound on an fp8 cache, before its P carried the bf16
+rounding remainder)."""
+
+import os
 
 import numpy as np
 import pytest
@@ -30,19 +37,28 @@ def _case(seed):
         lens[int(rng.integers(0, B))] = int(rng.choice([0, 1]))
     S = int(rng.choice([1, 2, 3, 8, 17]))
     partition = int(rng.choice([0, 1, 2]))
-    return index, H, lens, S, partition
+    # stage-1 choice, from its own generator so the draws above stay as they were
+    r2 = np.random.default_rng(5000 + seed)
+    mode = r2.choice(["default", "token_split", "length_classes"], p=[0.5, 0.25, 0.25])
+    opts = {}
+    if mode == "token_split" and index != 4 and H % 16 == 0:      # bf16 cache
+        opts = dict(kernel=3, heads_per_group=32 if H % 32 == 0 and r2.random() < 0.5 else 16)
+    elif mode == "length_classes" and index != 4 and H % 32 == 0:
+        S, partition = 1, 0
+        opts = dict(split_len=int(r2.choice([1, 300, 1000])))
+    return index, H, lens, S, partition, opts
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(int(os.environ.get("MLA_RANDOM_CASES", "100"))))
 def test_random_configuration_against_oracle(seed):
-    index, H, lens, S, partition = _case(seed)
-    print(f"[random {seed}] workload {index} H={H} S={S} partition={partition} lens={lens}", flush=True)
+    index, H, lens, S, partition, opts = _case(seed)
+    print(f"[random {seed}] workload {index} H={H} S={S} partition={partition} {opts} lens={lens}", flush=True)
     bt = W.make_batch(index, DEV, seq_lens=lens, H=H, seed=seed)
     ref_cache = oracle_cache(bt)
     M.cache_write(bt.kv_c, bt.k_pe, bt.cache, bt.slot_mapping, "fp8" if bt.spec.cache_dtype == "fp8" else "auto",
                   bt.scale)
     o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
     o, lse = M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, SM, S, bt.spec.R, kv_scale=bt.scale,
-                      partition=partition)
+                      partition=partition, **opts)
     torch.cuda.synchronize()
     compare(o, lse, o_ref, lse_ref, bt.spec.in_dtype)
