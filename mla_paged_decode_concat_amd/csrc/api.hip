@@ -334,6 +334,10 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
   // XCD and still finds the lines); tiles shared by more groups are meant to
   // meet in L2
   p.kv_nt = groups <= 2 ? 1 : 0;
+  // one partial per request: the matrix-core stage 1 writes o and lse
+  // itself (the merge of a single partial is the identity, bit for bit), so
+  // there is no stage 2 and no workspace traffic
+  p.direct = use_mfma && num_kv_splits == 1 ? 1 : 0;
   hipError_t e;
   if (split_len > 0) {
     DecodeParams pt = p;
@@ -349,8 +353,10 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
                : launch_stage1_valu(q_dtype, cache_dtype, kv_lora_rank, p, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
   if (ev[1] && hipEventRecord(ev[1], st) != hipSuccess) return MLA_ERR_HIP;
-  e = launch_stage2(q_dtype, kv_lora_rank, p, st);
-  if (e != hipSuccess) return MLA_ERR_HIP;
+  if (!p.direct) {
+    e = launch_stage2(q_dtype, kv_lora_rank, p, st);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+  }
   if (ev[2] && hipEventRecord(ev[2], st) != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }

@@ -694,11 +694,20 @@ struct Stage1 {
       const float inv = kvs / lm;
       const float lse = (m_ref[nb] + __builtin_amdgcn_logf(l)) * kLn2;
       const int h = head0 + 16 * nb + r16;
-      float* dst = ws_row(p, part, h, R);
+      if (p.direct) {   // one branch for the whole row, not one per store
 #pragma unroll
-      for (int cb = 0; cb < G::CB; ++cb)
-        *reinterpret_cast<f32x4_t*>(dst + 16 * cb + 4 * g) = acc[cb][nb] * inv;
-      if (g == 0) *ws_lse(p, part, h, R) = lse;
+        for (int cb = 0; cb < G::CB; ++cb) {
+          const f32x4_t v = acc[cb][nb] * inv;
+          store_partial4<true>(p, b, part, h, R, 16 * cb + 4 * g, v[0], v[1], v[2], v[3]);
+        }
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < G::CB; ++cb) {
+          const f32x4_t v = acc[cb][nb] * inv;
+          store_partial4<false>(p, b, part, h, R, 16 * cb + 4 * g, v[0], v[1], v[2], v[3]);
+        }
+      }
+      if (g == 0) store_partial_lse(p, b, part, h, R, lse);
     }
   }
 };
@@ -931,17 +940,21 @@ struct Stage1TS {
       }
       const float inv = 1.0f / Lm;
       const int h = head0 + 16 * nb + r16;
-      float* dst = ws_row(p, part, h, R);
       constexpr int CPW = G::CB / 4;   // column blocks each wave writes
+      auto out = [&](auto direct) {
 #pragma unroll
-      for (int j = 0; j < CPW; ++j) {
-        const int cb = wave * CPW + j;
-        f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < CPW; ++j) {
+          const int cb = wave * CPW + j;
+          f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < 4; ++w) o += wt[w] * *MLA_LDS(const f32x4_t, mrg + ((w * G::CB + cb) * 64 + lane) * 4);
-        *reinterpret_cast<f32x4_t*>(dst + 16 * cb + 4 * g) = o * inv;
-      }
-      if (wave == 0 && g == 0) *ws_lse(p, part, h, R) = (M + __builtin_amdgcn_logf(Ls)) * kLn2;
+          for (int w = 0; w < 4; ++w) o += wt[w] * *MLA_LDS(const f32x4_t, mrg + ((w * G::CB + cb) * 64 + lane) * 4);
+          const f32x4_t v = o * inv;
+          store_partial4<decltype(direct)::value>(p, b, part, h, R, 16 * cb + 4 * g, v[0], v[1], v[2], v[3]);
+        }
+      };
+      if (p.direct) out(std::true_type{});
+      else out(std::false_type{});
+      if (wave == 0 && g == 0) store_partial_lse(p, b, part, h, R, (M + __builtin_amdgcn_logf(Ls)) * kLn2);
     }
     __syncthreads();   // the merge area is tile slots again for the next piece
   }
@@ -1006,6 +1019,14 @@ __global__ __launch_bounds__(K::NW_ * 64) void stage1_mfma_kernel(DecodeParams p
       const int kps = (n + p.S - 1) / p.S;
       a = s * kps;
       e = min(a + kps, n);
+      if (n <= 0 && p.direct && p.len_min <= 0) {
+        // an empty request has no piece: o = 0 and lse = -inf are written
+        // here when there is no stage 2 to write them
+        constexpr int R = K::G::D - 64;
+        uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.o) + ((long long)b * p.H + head0) * R);
+        for (int i = threadIdx.x; i < K::HPG * R / 8; i += K::NW_ * 64) o[i] = make_uint4(0, 0, 0, 0);
+        for (int i = threadIdx.x; i < K::HPG; i += K::NW_ * 64) p.lse[(long long)b * p.H + head0 + i] = -INFINITY;
+      }
       if (n <= 0 || e <= a || n < p.len_min || n >= p.len_max) break;
     } else {
       while (mask == 0) {

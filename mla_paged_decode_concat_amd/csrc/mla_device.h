@@ -216,6 +216,8 @@ struct DecodeParams {
   int heads_per_group;             // stage 1: heads per workgroup
   int token_split;                 // stage 1, 16- or 32-head groups: four waves split the tokens
   int kv_nt;                       // stage-1 tile loads carry the non-temporal hint (<= 2 head groups)
+  int direct;                      // one partial per request (num_kv_splits == 1): stage 1 writes o
+                                   // (bf16) and lse itself and stage 2 is not launched
   int len_min, len_max;            // literal partition: this stage-1 launch takes the requests
                                    // with len_min <= seq_len < len_max
 };
@@ -229,6 +231,28 @@ __device__ __forceinline__ float* ws_row(const DecodeParams& p, int slot, int h,
 }
 __device__ __forceinline__ float* ws_lse(const DecodeParams& p, int slot, int h, int R) {
   return p.ws + (long long)p.B * p.H * p.S * R + (long long)h * p.B * p.S + slot;
+}
+
+// Store four consecutive values of a head's partial output, columns
+// c .. c+3.  With one partial per request the partial is the result: the
+// merge would weight it by exp(0) = 1 and divide by 1, so it goes straight
+// to o (bf16, rounded to nearest even as the merge rounds it) instead of the
+// workspace.  DIRECT is p.direct, resolved by the caller once per row.
+template <bool DIRECT>
+__device__ __forceinline__ void store_partial4(const DecodeParams& p, int b, int slot, int h, int R, int c,
+                                               float x0, float x1, float x2, float x3) {
+  if constexpr (DIRECT) {
+    uint16_t* o = reinterpret_cast<uint16_t*>(p.o) + ((long long)b * p.H + h) * R + c;
+    *reinterpret_cast<uint2*>(o) =
+        make_uint2(f32_to_bf16_rne(x0) | (f32_to_bf16_rne(x1) << 16), f32_to_bf16_rne(x2) | (f32_to_bf16_rne(x3) << 16));
+  } else {
+    float* w = ws_row(p, slot, h, R) + c;
+    *reinterpret_cast<float4*>(w) = make_float4(x0, x1, x2, x3);
+  }
+}
+__device__ __forceinline__ void store_partial_lse(const DecodeParams& p, int b, int slot, int h, int R, float lse) {
+  if (p.direct) p.lse[(long long)b * p.H + h] = lse;
+  else *ws_lse(p, slot, h, R) = lse;
 }
 
 }  // namespace mla
