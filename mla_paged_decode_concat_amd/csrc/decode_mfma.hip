@@ -46,6 +46,7 @@
 #include "mla_device.h"
 #include "mla_launch.h"
 
+#include <type_traits>
 #include <utility>
 
 namespace mla {
@@ -88,7 +89,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // gptr + OFF and its bytes land at LDS address lds_base + 16 * i.  The
 // instruction's immediate offset is added to the LDS address too (M0 + OFF +
 // 16 i), so M0 is set to lds_base - OFF; callers keep lds_base >= OFF.  The
-// ISA asks for one wait state between writing M0 and the load.  Issued
+// ISA asks for one wait state between writing M0 and the load; M0 is
+// declared clobbered, so the compiler keeps nothing of its own there.  Issued
 // through inline asm so the compiler does not add a full vmcnt drain before
 // every later LDS read (it cannot prove the in-flight tile and the tile being
 // read are disjoint); the kernel orders them itself with wait_vmcnt + a
@@ -110,11 +112,11 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
   if constexpr (NT)
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2 nt" ::"v"(gptr), "s"(m0),
                  "i"(OFF)
-                 : "memory");
+                 : "memory", "m0");
   else
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2" ::"v"(gptr), "s"(m0),
                  "i"(OFF)
-                 : "memory");
+                 : "memory", "m0");
 }
 
 // This lane's index, read so that the compiler cannot hoist what is derived
@@ -712,6 +714,370 @@ struct Stage1 {
   }
 };
 
+// Stage 1 for a 128-head group on a bf16 cache, with two waves per SIMD in
+// different roles.  One wave per SIMD cannot keep its SIMD's matrix core busy:
+// its LDS reads wait out their latency, its softmax leaves the matrix core
+// idle, and a tile-load issue that finds the CU's load queue full stalls it.
+// Here SIMD j runs two waves for the 32 heads 32j .. 32j+31:
+//  * the QK wave (waves 0-3) holds Q for its heads in registers, computes
+//    S^T = K Q^T over the tile, the softmax (fixed reference, as in Stage1),
+//    writes P (bf16, the matrix cores' B-operand layout) to LDS and
+//    accumulates value columns 0 .. 16*CA-1 itself;
+//  * the PV wave (waves 4-7) accumulates the other value columns, one tile
+//    behind: in the interval in which the QK wave works on tile k it reads
+//    P(k-1) and tile k-1's V^T, and it issues all of the tile loads (its
+//    token quarter of tile k+2), so a stalled load issue never holds up the
+//    QK chain.
+// While one wave of a SIMD runs vector code or waits on LDS the other one
+// feeds the matrix core.  One workgroup barrier per tile orders everything:
+// after barrier k, tile k has landed, P(k-1) is written, and the ring slots
+// of tiles k-2 (values) and k-1 (rope columns) are free.  The value columns
+// of a tile sit in a 4-slot ring (read by the QK wave in interval k and by
+// the PV wave in interval k+1), the rope columns in a 3-slot ring (QK only).
+// Every head's accumulation order is the one Stage1 uses, so the results are
+// the same bits.
+template <int R, int CA, int KRING = 3, int VRA = 3, int VRB = 3>
+struct Stage1AB {
+  using G = Geo<R>;
+  using TL = TileLoad<R, 4>;
+  static constexpr int NW_ = 8;
+  static constexpr int HPG = 128;
+  static constexpr int CB = G::CB;                 // value column blocks of 16
+  static constexpr int CBB = CB - CA;              // the PV wave's share
+  static_assert(CA >= 1 && CBB >= 1, "column split");
+  static constexpr int LPW = G::NBLK / 4;          // load instructions per PV wave per tile
+  static constexpr int VKS = R / 32;               // QK k-steps over the value columns
+  static constexpr int VSLOT = (G::CHUNKS / 8 - 1) * 4096;
+  static constexpr int RSLOT = 4096;
+  static constexpr int NV = 4, NR = 3;
+  static constexpr int P_OFF = NV * VSLOT + NR * RSLOT;
+  static constexpr int PBUF = HPG * kTile * 2;     // P of one tile, bf16
+  static constexpr int SMEM = P_OFF + 2 * PBUF;
+  static constexpr int TABLE = R == 512 ? 1016 : kTableWindow;
+  // LDS read-ahead depths (ring slots): K rows in QK, V^T in each wave's PV
+  static constexpr int kKRing = KRING, kVRingA = VRA, kVRingB = VRB;
+  static_assert(SMEM + TABLE * 4 + 8 <= 160 * 1024, "LDS");
+
+  static __device__ __forceinline__ char* vslot(char* smem, int t) { return smem + (t % NV) * VSLOT; }
+  static __device__ __forceinline__ char* rslot(char* smem, int t) { return smem + NV * VSLOT + (t % NR) * RSLOT; }
+  static __device__ __forceinline__ char* pbuf(char* smem, int t, int hg) {
+    return smem + P_OFF + (t & 1) * PBUF + hg * 2048;
+  }
+
+  template <bool NT>
+  static __device__ __forceinline__ void issue(const DecodeParams& p, int sa, int t, int se, int pg0, char* smem,
+                                               const int* s_table, int hg) {
+    const typename TL::Rows rw = TL::rows(p, sa + kTile * t, se, pg0, s_table, hg);
+    char* vb = vslot(smem, t);
+    char* rb = rslot(smem, t);
+    static_for<LPW>([&](auto i) { TL::template issue<decltype(i)::value, NT>(rw, vb, rb, hg); });
+  }
+
+  template <bool NT>
+  static __device__ void piece(const DecodeParams& p, int b, int a, int e, int part, int head0,
+                               char* smem, int* s_table, int* s_flags) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (wave < 4) run<true, NT>(p, b, a, e, part, head0, wave, smem, s_table, s_flags);
+    else run<false, NT>(p, b, a, e, part, head0, wave - 4, smem, s_table, s_flags);
+  }
+
+  // QK wave, one tile: S^T = K Q^T, the softmax, P(k) to LDS for the PV
+  // wave, and this wave's own value columns.  Returns nothing; updates the
+  // softmax state and may flag a redo.
+  template <int KR>
+  static __device__ __forceinline__ void qk_tile(const bf16x8_t (&qf)[2][G::KS], f32x4_t (&acc)[CA][2],
+                                                 float (&m_ref)[2], float (&l_sum)[2], float (&l_mma)[2],
+                                                 float (&m_init)[2], const char* vt, const char* rt, char* pb,
+                                                 int tile_start, int se, float c2, int* flag) {
+    const int lane = lane_now();
+    const int g = lane >> 4, r16 = lane & 15;
+    // K rows: token r16 of a 16-token block, chunk 4 * (ks & 1) + g of the
+    // block's 8 column chunks (swizzled); the block part is an immediate
+    const int t8 = r16 & 7, tqo = r16 >> 3;
+    const uint32_t k0 = lds_addr(vt) + (uint32_t)(tqo * 1024 + (8 * t8 + ((g) ^ TL::swz(t8, tqo))) * 16);
+    const uint32_t k1 = lds_addr(vt) + (uint32_t)(tqo * 1024 + (8 * t8 + ((4 + g) ^ TL::swz(t8, tqo))) * 16);
+    const uint32_t kr0 = k0 - lds_addr(vt) + lds_addr(rt), kr1 = k1 - lds_addr(vt) + lds_addr(rt);
+    auto kread = [&](int ks, int mb) -> bf16x8_t {
+      const uint32_t base = ks < VKS ? ((ks & 1) ? k1 : k0) : ((ks & 1) ? kr1 : kr0);
+      const uint32_t off = ks < VKS ? ((ks >> 1) * 4 + 2 * mb) * 1024 : (2 * mb) * 1024;
+      return *MLA_LDS(const bf16x8_t, (uintptr_t)(base + off));
+    };
+    f32x4_t s[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) s[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t kr[KR][2];
+#pragma unroll
+    for (int ks = 0; ks < KR - 1; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) kr[ks][mb] = kread(ks, mb);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<G::KS>([&](auto KSI) {
+      constexpr int ks = decltype(KSI)::value;
+      if (ks + KR - 1 < G::KS) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) kr[(ks + KR - 1) % KR][mb] = kread(ks + KR - 1, mb);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          s[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks % KR][mb], qf[nb][ks], s[mb][nb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+
+    // softmax in the log2 domain; lane owns head r16, tokens 16mb + 4g + i.
+    // Tokens past the range (only in a range's last tile) score -inf.
+    bool need = false;
+    float mt[2];
+    const bool full = tile_start + kTile <= se;   // the same for the whole wave
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      mt[nb] = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = tile_start + 16 * mb + 4 * g + i;
+          const float v = full || tok < se ? s[mb][nb][i] * c2 : -INFINITY;
+          s[mb][nb][i] = v;
+          mt[nb] = fmaxf(mt[nb], v);
+        }
+      need |= mt[nb] > m_ref[nb] + kSlack;    // also true while m_ref is unset (-inf)
+    }
+    if (__builtin_expect(__any(need), 0)) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float m = mt[nb];
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        if (m_ref[nb] == -INFINITY) {
+          m_ref[nb] = m;                     // first tile of the pass
+        } else if (m > m_ref[nb] + kSlack) {
+          m_init[nb] = m;                    // not representable in this pass
+          *flag = 1;
+        }
+      }
+    }
+    bf16x8_t pf[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float ls = 0.0f, lm = 0.0f;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pj = __builtin_amdgcn_exp2f(s[mb][nb][i] - m_ref[nb]);
+          const __bf16 pb = (__bf16)pj;
+          ls += pj;
+          pf[nb][4 * mb + i] = pb;
+          lm += (float)pb;
+        }
+      l_sum[nb] += ls;
+      l_mma[nb] += lm;
+    }
+    // P(k) for the PV wave of this SIMD (read after the next barrier)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) *MLA_LDS(bf16x8_t, pb + nb * 1024 + lane * 16) = pf[nb];
+    pv<CA, 0, kVRingA>(acc, vt, pf);
+  }
+
+  // O^T += V^T P^T over column blocks CB0 .. CB0+N-1 of one tile; V^T read
+  // two column blocks ahead through a 3-slot ring (transpose reads: this
+  // lane addresses token 16tb + 4g + (r16 >> 2), bytes [8 (r16 & 3), +8) of
+  // a 16-column block)
+  template <int N, int CB0, int VR>
+  static __device__ __forceinline__ void pv(f32x4_t (&acc)[N][2], const char* vt, const bf16x8_t (&pf)[2]) {
+    const int lane = lane_now();
+    const int g = lane >> 4, r16 = lane & 15;
+    const int sg = r16 & 3;
+    const int t8 = 4 * (g & 1) + (r16 >> 2), tqo = g >> 1;
+    // lane part for column blocks with cb & 3 == j is vb + 32 * j (the chunk
+    // index 2j + (sg >> 1) enters the swizzle), so keep the four as one base
+    // plus per-j terms
+    uint32_t voff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      voff[j] = lds_addr(vt) + (uint32_t)(tqo * 1024 + (8 * t8 + ((2 * j + (sg >> 1)) ^ TL::swz(t8, tqo))) * 16 +
+                                          (sg & 1) * 8);
+    auto vread = [&](int cb) -> bf16x8_t {
+      const uint32_t a0 = voff[cb & 3] + (cb >> 2) * 4096;
+      const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(MLA_LDS(bf16x4_t, (uintptr_t)a0));
+      const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(MLA_LDS(bf16x4_t, (uintptr_t)(a0 + 2048)));
+      return bf16x8_t{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8_t vr[VR];
+#pragma unroll
+    for (int c = 0; c < VR - 1; ++c)
+      if (c < N) vr[c] = vread(CB0 + c);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<N>([&](auto CI) {
+      constexpr int c = decltype(CI)::value;
+      if (c + VR - 1 < N) vr[(c + VR - 1) % VR] = vread(CB0 + c + VR - 1);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        acc[c][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[c % VR], pf[nb], acc[c][nb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+
+  template <bool QKW, bool NT>
+  static __device__ __forceinline__ void run(const DecodeParams& p, int b, int a, int e, int part, int head0, int hg,
+                                             char* smem, int* s_table, int* s_flags) {
+    const int hb = head0 + 32 * hg;                // this SIMD's heads hb .. hb+31
+    constexpr int NACC = QKW ? CA : CBB;
+    constexpr int CB0 = QKW ? 0 : CA;              // first column block this wave accumulates
+
+    // Q^T operand (QK wave): lane = head r16 of block nb, dims 32ks + 8g .. +8
+    bf16x8_t qf[2][G::KS];
+    if constexpr (QKW) {
+      const int lane = threadIdx.x & 63;
+      const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + (long long)b * p.q_sb;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int h = hb + 16 * nb + (lane & 15);
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks)
+          qf[nb][ks] = *reinterpret_cast<const bf16x8_t*>(qb + (long long)h * p.q_sh + 32 * ks + 8 * (lane >> 4));
+      }
+      wait_vmcnt<0>();
+    }
+
+    f32x4_t acc[NACC][2];
+    float m_ref[2], l_sum[2], l_mma[2], m_init[2] = {-INFINITY, -INFINITY};
+    const float c2 = p.sm_scale * kLog2e;
+    auto reset = [&]() {
+#pragma unroll
+      for (int c = 0; c < NACC; ++c)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[c][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        m_ref[nb] = m_init[nb];
+        l_sum[nb] = 0.0f;
+        l_mma[nb] = 0.0f;
+      }
+    };
+    reset();
+
+    const int bs = p.block_size;
+    const int32_t* btab = p.block_table + (long long)b * p.bt_stride;
+    // One block-table window at a time.  Softmax reference: each head's is
+    // fixed by its first tile of the pass and p = 2^(s - m_ref) is summed
+    // unscaled; a later tile more than kSlack above it makes every wave zero
+    // its state and rewind to a with the larger reference (each redo raises
+    // a reference by more than kSlack, so this ends).
+#pragma unroll 1
+    for (int sa = a; sa < e;) {
+      const int pg0 = sa / bs;
+      const long long win_end = (long long)(pg0 + TABLE) * bs;
+      int se = e;
+      if (win_end < e) se = sa + (int)((win_end - sa) / kTile) * kTile;
+      __syncthreads();   // earlier readers of s_table, s_flags and the ring are done
+      const int npg = (se - 1) / bs - pg0 + 1;
+      for (int i = threadIdx.x; i < npg; i += NW_ * 64) s_table[i] = btab[pg0 + i];
+      if (threadIdx.x == 0) {
+        s_flags[0] = 0;
+        s_flags[1] = 0;
+      }
+      __syncthreads();
+
+      const int T = (se - sa + kTile - 1) / kTile;
+      // No load of this wave is in flight here.  Saying so to the compiler
+      // (it does not see the tile loads, which are inline asm) keeps it from
+      // guarding registers that an earlier load wrote with a full vmcnt wait
+      // inside the tile loop, which would also drain the tile loads.
+      wait_vmcnt<0>();
+      if constexpr (!QKW) {
+        issue<NT>(p, sa, 0, se, pg0, smem, s_table, hg);
+        if (T > 1) issue<NT>(p, sa, 1, se, pg0, smem, s_table, hg);
+      }
+      bool redo = false;
+#pragma unroll 1
+      for (int k = 0; k <= T; ++k) {
+        if constexpr (!QKW) {
+          // tile k landed (tile k+1 may still be in flight)
+          if (k + 1 < T) wait_vmcnt<LPW>();
+          else wait_vmcnt<0>();
+        }
+        __syncthreads();
+        // a redo flagged while computing tile k-1 is seen by all waves here
+        if (k > 0 && s_flags[(k - 1) & 1]) {
+          redo = true;
+          break;
+        }
+        if constexpr (QKW) {
+          if (k < T)
+            qk_tile<kKRing>(qf, acc, m_ref, l_sum, l_mma, m_init, vslot(smem, k), rslot(smem, k), pbuf(smem, k, hg),
+                       sa + kTile * k, se, c2, &s_flags[k & 1]);
+        } else {
+          if (k >= 1) {
+            const int lane = lane_now();
+            bf16x8_t pf[2];
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+              pf[nb] = *MLA_LDS(const bf16x8_t, pbuf(smem, k - 1, hg) + nb * 1024 + lane * 16);
+            pv<CBB, CA, kVRingB>(acc, vslot(smem, k - 1), pf);
+          }
+          // Tile k+2 after this wave's PV: by now tile k+1 has mostly
+          // landed, so the issue does not stall on a full load queue (issued
+          // first, it held the PV back by about a thousand cycles), and it
+          // still has about one and a half intervals to land.
+          if (k + 2 < T) issue<NT>(p, sa, k + 2, se, pg0, smem, s_table, hg);
+        }
+      }
+      wait_vmcnt<0>();     // nothing may still be landing when the ring is reused
+      if (redo) {
+        reset();
+        sa = a;
+      } else {
+        sa = se;
+      }
+    }
+
+    // ---- finalize: the QK wave owns the softmax sums; it hands 1 / l to the PV wave
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, r16 = lane & 15;
+    __syncthreads();         // every wave is done with the ring and the P buffers
+    float* s_inv = reinterpret_cast<float*>(smem);
+    float inv[2];
+    if constexpr (QKW) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float l = l_sum[nb], lm = l_mma[nb];
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        lm += __shfl_xor(lm, 16, 64);
+        lm += __shfl_xor(lm, 32, 64);
+        inv[nb] = 1.0f / lm;
+        if (g == 0) {
+          s_inv[hg * 32 + 16 * nb + r16] = inv[nb];
+          store_partial_lse(p, b, part, hb + 16 * nb + r16, R, (m_ref[nb] + __builtin_amdgcn_logf(l)) * kLn2);
+        }
+      }
+    }
+    __syncthreads();
+    if constexpr (!QKW) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) inv[nb] = s_inv[hg * 32 + 16 * nb + r16];
+    }
+    // one column block at a time, so the products need no more registers
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int h = hb + 16 * nb + r16;
+#pragma unroll
+      for (int c = 0; c < NACC; ++c) {
+        const f32x4_t v = acc[c][nb] * inv[nb];
+        if (p.direct) store_partial4<true>(p, b, part, h, R, 16 * (CB0 + c) + 4 * g, v[0], v[1], v[2], v[3]);
+        else store_partial4<false>(p, b, part, h, R, 16 * (CB0 + c) + 4 * g, v[0], v[1], v[2], v[3]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+};
+
 // Token-split stage 1 for one group of 16 * NB heads (bf16 cache).  When
 // the token ranges are few (the partial-slot cap binds, or the literal
 // partition has fewer items than CUs), a workgroup whose waves share each
@@ -978,33 +1344,53 @@ __host__ __device__ inline int mapped_grid(int items, int groups) {
   return ((items + kXcds - 1) / kXcds) * kXcds * groups;
 }
 
+// Inclusive prefix sum across the wave, 32-bit.  The lane index is read
+// through lane_now() so that its derived shuffle indices are not hoisted and
+// kept live around the caller's loops.
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v) {
+  const int ln = lane_now();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t t = (uint32_t)__builtin_amdgcn_ds_bpermute((ln - o) << 2, (int)v);
+    if (ln >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ long long uniform64(long long v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
 template <class K, bool NT>
 __global__ __launch_bounds__(K::NW_ * 64) void stage1_mfma_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[K::SMEM];
   __shared__ int s_table[K::TABLE];
   __shared__ int s_flags[2];
-  const int lane = threadIdx.x & 63;
   const int groups = p.H / K::HPG;
 
   // Enumerate this workgroup's pieces (request, token range, partial index)
-  // and run each; piece() is inlined at one call site only.
+  // and run each; piece() is inlined at one call site only.  Between pieces
+  // only wave-uniform values (scalar registers) and two values per lane stay
+  // live, so the pieces keep the vector registers.
   const bool literal = p.partition == PART_LITERAL;
   int item, hg;
   if (!map_block(blockIdx.x, literal ? p.B * p.S : p.G, groups, item, hg)) return;
   const int head0 = hg * K::HPG;
-  long long Q = 0, lo = 0, hi = 0, carry = 0;
+  long long lo = 0, hi = 0, carry = 0;
   int base = 0;
   unsigned long long mask = 0;
-  long long start = 0, incl = 0;
-  int nlane = 0;
+  int d_lane = 0, n_lane = 0;      // per lane of the scanned block: padded start - lo, length
   bool done = false;
   if (literal) {
     lo = item;   // the single (request, split) of this workgroup
   } else {
-    const BatchTotals t = batch_totals(p.seq_lens, p.B, lane);
-    Q = balanced_chunk(t, p.G);
+    const BatchTotals t = batch_totals(p.seq_lens, p.B, lane_now());
+    const long long total = uniform64(t.total);
+    const long long Q = balanced_chunk(BatchTotals{total, 0}, p.G);
     lo = (long long)item * Q;
-    hi = min(lo + Q, t.total);
+    hi = min(lo + Q, total);
     done = lo >= hi;
     base = -kWave;
   }
@@ -1030,24 +1416,26 @@ __global__ __launch_bounds__(K::NW_ * 64) void stage1_mfma_kernel(DecodeParams p
       if (n <= 0 || e <= a || n < p.len_min || n >= p.len_max) break;
     } else {
       while (mask == 0) {
-        if (base >= 0) carry += __shfl(incl, kWave - 1, kWave);
         base += kWave;
         if (base >= p.B || carry >= hi) break;
-        const int bb = base + lane;
-        nlane = bb < p.B ? max(p.seq_lens[bb], 0) : 0;
-        const long long n32 = pad32(nlane);
-        incl = wave_scan_i64(n32, lane);
-        start = carry + incl - n32;
-        mask = __ballot(nlane > 0 && start < hi && start + nlane > lo);
+        const int bb = base + lane_now();
+        const int n = bb < p.B ? max(p.seq_lens[bb], 0) : 0;
+        const uint32_t u = (uint32_t)((n + 31) >> 5);          // padded length in 32-token units
+        const uint32_t incl = wave_scan_u32(u);
+        const long long st = carry + 32LL * (long long)(incl - u);
+        mask = __ballot(n > 0 && st < hi && st + n > lo);
+        d_lane = (int)(st - lo);                               // used only where the mask is set
+        n_lane = n;
+        carry += 32LL * (long long)__builtin_amdgcn_readlane(incl, kWave - 1);
       }
       if (mask == 0) break;
       const int j = __ffsll((long long)mask) - 1;
       mask &= mask - 1;
-      const long long st = __shfl(start, j, kWave);
-      const int nn = __shfl(nlane, j, kWave);
+      const int d = __builtin_amdgcn_readlane(d_lane, j);
+      const int nn = __builtin_amdgcn_readlane(n_lane, j);
       b = base + j;
-      a = (int)(lo > st ? lo - st : 0);
-      e = (int)min(hi - st, (long long)nn);
+      a = d < 0 ? -d : 0;
+      e = min((int)(hi - lo) - d, nn);
       part = item + b;                     // slot of the piece (chunk item, request b)
     }
     // the piece is the same for every lane: say so, so that its bounds and
@@ -1099,10 +1487,17 @@ constexpr int stages_for() {
 template <class K>
 constexpr int lds_bytes() { return K::SMEM + K::TABLE * (int)sizeof(int) + 2 * (int)sizeof(int); }
 
+// the 128-head kernel for an R = 512 bf16 cache, and its column split
+template <int R, bool F8>
+struct Wide {
+  static constexpr bool AB = R == 512 && !F8;
+  using K = typename std::conditional<AB, Stage1AB<R, 5, 2, 2, 2>, Stage1<R, 2, 4, stages_for<R, 4, F8>(), F8>>::type;
+};
+
 template <int R, bool F8>
 static int lds_bytes_r(int hpg) {
   switch (hpg) {
-    case 128: return lds_bytes<Stage1<R, 2, 4, stages_for<R, 4, F8>(), F8>>();
+    case 128: return lds_bytes<typename Wide<R, F8>::K>();
     case 64: return lds_bytes<Stage1<R, 2, 2, stages_for<R, 2, F8>(), F8>>();
     case 32: return lds_bytes<Stage1<R, 2, 1, stages_for<R, 1, F8>(), F8>>();
     default: return lds_bytes<Stage1<R, 1, 1, stages_for<R, 1, F8>(), F8>>();
@@ -1115,7 +1510,7 @@ int mfma_wgs_per_cu(int hpg, int R, int cache_dtype, int lds_per_cu) {
   const bool f8 = cache_dtype == DT_FP8;
   const int lds = R == 512 ? (f8 ? lds_bytes_r<512, true>(hpg) : lds_bytes_r<512, false>(hpg))
                            : (f8 ? lds_bytes_r<256, true>(hpg) : lds_bytes_r<256, false>(hpg));
-  const int waves = hpg >= 128 ? 4 : hpg == 64 ? 2 : 1;
+  const int waves = hpg >= 128 ? 4 : hpg == 64 ? 2 : 1;   // SIMDs a workgroup's waves occupy
   int n = lds_per_cu / lds;
   if (n > 4 / waves) n = 4 / waves;
   return n < 1 ? 1 : n;
@@ -1136,7 +1531,7 @@ static hipError_t launch_k(const DecodeParams& p, hipStream_t stream) {
 template <int R, bool F8>
 static hipError_t launch_r(const DecodeParams& p, hipStream_t stream) {
   switch (p.heads_per_group) {
-    case 128: return launch_k<Stage1<R, 2, 4, stages_for<R, 4, F8>(), F8>>(p, stream);
+    case 128: return launch_k<typename Wide<R, F8>::K>(p, stream);
     case 64: return launch_k<Stage1<R, 2, 2, stages_for<R, 2, F8>(), F8>>(p, stream);
     case 32:
       if constexpr (!F8)

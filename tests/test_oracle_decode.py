@@ -351,3 +351,41 @@ def test_decode_multi_token_rows_attend_to_whole_sequence():
     o1, l1 = O.decode_multi_token(q[:, :1], cache, table, lens, sm, "f32", "f32", R)
     o0, l0 = O.decode(q[:, 0], cache, table, lens, sm, "f32", "f32", R)
     assert np.array_equal(o1[:, 0], o0) and np.array_equal(l1[:, 0], l0)
+
+
+@pytest.mark.parametrize("index,kw", [(0, {}), (1, dict(B=5, max_len=700)), (3, dict(B=4, max_len=300)),
+                                      (4, dict(B=3, max_len=1100))])
+def test_decode_split_merge_equals_unsplit_decode(index, kw):
+    """The two-stage pipeline with the pages' partition (ceil(n/S) tokens per
+    split, empty splits skipped, LSE merge) reaches the unsplit decode for
+    every split count, including one- and zero-token requests ("fix TP" diff,
+    triton_decode_attention.py: stage-1 split range and the stage-2 skip of
+    empty splits)."""
+    bt = W.make_batch(index, "cpu", **kw)
+    spec = bt.spec
+    scale = float(bt.scale[0]) if bt.scale is not None else None
+    cache = O.cache_write(W.bits(bt.cache), W.bits(bt.kv_c), W.bits(bt.k_pe), bt.slot_mapping.numpy(),
+                          spec.in_dtype, spec.cache_dtype, scale)
+    lens = bt.seq_lens.numpy().copy()
+    lens[0] = 1                       # one token: a single split whatever S is
+    if len(lens) > 2:
+        lens[-1] = 0                  # empty request: o = 0, lse = -inf
+    args = (W.bits(bt.q), cache, bt.block_table.numpy(), lens, W.SM_SCALE, spec.in_dtype, spec.cache_dtype, spec.R)
+    o, lse = O.decode(*args, scale)
+    for S in [1, 2, 3, 7, 16, int(lens.max())]:
+        o2, l2 = O.decode_split_merge(*args, S, scale)
+        fin = np.isfinite(lse)
+        assert np.array_equal(np.isfinite(l2), fin)
+        assert np.all(l2[~fin] == -np.inf) and np.all(o2[~fin] == 0.0)
+        assert np.max(np.abs(o2 - o)) < 1e-12
+        assert np.max(np.abs(l2[fin] - lse[fin])) < 1e-12
+
+
+def test_workspace_floats_hand_values():
+    """[B, H, S, R+1] fp32 elements ("Triton and MLA" essay, Data flow: the
+    attn_logits workspace; API page: _reserve_attn_logits_workspace), worked
+    out by hand for the V3 per-GPU shape: 64*128*16*513 and 64*128*1*513."""
+    assert O.workspace_floats(64, 128, 16, 512) == 67_239_936
+    assert O.workspace_floats(64, 128, 1, 512) == 4_202_496
+    assert O.workspace_floats(2, 4, 2, 512) == 8_208
+    assert O.workspace_floats(128, 32, 64, 256) == 67_371_008
