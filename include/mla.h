@@ -344,6 +344,36 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
                   const mla_decode_opts_t* opts);
 
 /*
+ * mla_decode without a caller-provided workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The split partials go to a scratch array
+ * the library keeps on each GPU for the life of the process
+ * (MLA_NOALLOC_SCRATCH_BYTES, allocated when the library's device code is
+ * first loaded on that GPU); this call allocates nothing itself.
+ *   Arguments, results, layouts and ownership: as mla_decode, minus
+ *   workspace and workspace_bytes.  The results are the same bits as
+ *   mla_decode's for the same arguments.
+ *   Limit: mla_decode_workspace_bytes(B, H, num_kv_splits, kv_lora_rank) must
+ *   not exceed MLA_NOALLOC_SCRATCH_BYTES, else MLA_ERR_WORKSPACE before any
+ *   launch (a smaller num_kv_splits needs less).
+ *   Every call on one GPU uses that GPU's one scratch array: calls that can
+ *   overlap on a GPU (different streams without ordering between them, or
+ *   different host threads) race and must be serialised by the caller.
+ * Errors: as mla_decode, plus MLA_ERR_HIP when the scratch array cannot be
+ * located on the current device.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int mla_decode_noalloc(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_dtype,
+                       int B, int H,
+                       const void* cache, int cache_dtype, int64_t num_blocks, int block_size,
+                       int64_t block_stride, int kv_lora_rank, int rope_dim,
+                       const int32_t* block_table, int64_t block_table_stride, int max_blocks_per_seq,
+                       const int32_t* seq_lens,
+                       float sm_scale, const float* kv_scale,
+                       int num_kv_splits,
+                       void* o, float* lse, void* stream);
+
+/*
  * Merge of partial attention results over disjoint key sets: combining the
  * per-shard outputs of a request whose tokens are split across GPUs (decode
  * context parallelism), here on one GPU's buffers.  For every (b, h):

@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     MLAError,
     cache_write,
     decode,
+    decode_noalloc,
     decode_workspace_bytes,
     library_path,
     linear,

@@ -21,7 +21,7 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace too
 
 EXPORTS = ["mla_status_string", "mla_num_kv_splits", "mla_decode_workspace_bytes", "mla_cache_write",
            "mla_decode", "mla_decode_ex", "mla_merge_partials", "mla_cache_write_rope", "mla_rope_q",
-           "mla_linear_bf16", "mla_linear_workspace_bytes"]
+           "mla_linear_bf16", "mla_linear_workspace_bytes", "mla_decode_noalloc"]
 
 
 class MLAError(RuntimeError):
@@ -66,6 +66,8 @@ def load_library():
            vp, sz, vp, vp, vp]
     lib.mla_decode.restype = i32
     lib.mla_decode.argtypes = dec
+    lib.mla_decode_noalloc.restype = i32
+    lib.mla_decode_noalloc.argtypes = dec[:20] + [vp, vp, vp]
     lib.mla_decode_ex.restype = i32
     lib.mla_decode_ex.argtypes = dec + [ctypes.POINTER(DecodeOpts)]
     lib.mla_cache_write_rope.restype = i32
@@ -239,30 +241,11 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
     B, H, D = q.shape
     R = kv_lora_rank
     P = D - R
-    if q.stride(-1) != 1 or kv_cache.stride(-1) != 1 or kv_cache.stride(1) != kv_cache.shape[2]:
-        raise ValueError("rows must be contiguous")
-    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
-        raise TypeError("block_table and seq_lens must be int32 (seq_lens contiguous)")
-    if block_table.stride(-1) != 1:
-        raise ValueError("block_table rows must be contiguous")
-    if seq_lens.numel() != B or block_table.dim() != 2 or block_table.shape[0] < B:
-        raise ValueError("seq_lens must hold B entries and block_table B rows")
-    if kv_cache.dim() != 3 or kv_cache.shape[2] != D:
-        raise ValueError("kv_cache must be [num_blocks, block_size, R + P]")
-    if kv_scale is not None and kv_scale.numel() < 1:
-        raise ValueError("kv_scale must hold one fp32 value")
     lib = load_library()
-    if o is None:
-        o = torch.empty((B, H, R), dtype=q.dtype, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    o, lse = _decode_outputs(q, kv_cache, block_table, seq_lens, kv_scale, o, lse, R)
     need = lib.mla_decode_workspace_bytes(max(B, 1), H, num_kv_splits, R)
     if workspace is None:
         workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=q.device)
-    if not (o.is_contiguous() and lse.is_contiguous() and lse.dtype == torch.float32 and o.dtype == q.dtype):
-        raise ValueError("o must be contiguous in q's dtype and lse contiguous fp32")
-    if tuple(o.shape) != (B, H, R) or tuple(lse.shape) != (B, H):
-        raise ValueError("o must be [B, H, R] and lse [B, H]")
     _same_gpu(q, kv_cache, block_table, seq_lens, kv_scale, workspace, o, lse)
     opts = DecodeOpts(partition, kernel, grid, heads_per_group)
     opts.split_len = split_len
@@ -277,6 +260,55 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), o.data_ptr(), lse.data_ptr(),
         _stream(q.device), ctypes.byref(opts))
     _check(st, "mla_decode")
+    return o, lse
+
+
+def decode_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                   sm_scale: float, num_kv_splits: int, kv_lora_rank: int = 512,
+                   kv_scale: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """decode through mla_decode_noalloc: the split partials go to the
+    library's per-GPU scratch array, so the library call allocates nothing
+    (o and lse are allocated here only when not given).  q is [B, H, R+P]."""
+    B, H, D = q.shape
+    R = kv_lora_rank
+    lib = load_library()
+    o, lse = _decode_outputs(q, kv_cache, block_table, seq_lens, kv_scale, o, lse, R)
+    _same_gpu(q, kv_cache, block_table, seq_lens, kv_scale, o, lse)
+    st = lib.mla_decode_noalloc(
+        q.data_ptr(), q.stride(0), q.stride(1), _dtype_code(q), B, H,
+        kv_cache.data_ptr(), _dtype_code(kv_cache), kv_cache.shape[0], kv_cache.shape[1], kv_cache.stride(0),
+        R, D - R, block_table.data_ptr(), block_table.stride(0), block_table.shape[1], seq_lens.data_ptr(),
+        float(sm_scale), kv_scale.data_ptr() if kv_scale is not None else None, int(num_kv_splits),
+        o.data_ptr(), lse.data_ptr(), _stream(q.device))
+    _check(st, "mla_decode_noalloc")
+    return o, lse
+
+
+def _decode_outputs(q, kv_cache, block_table, seq_lens, kv_scale, o, lse, R):
+    """Argument checks shared by the decode calls; returns (o, lse), new
+    tensors where None was given."""
+    B, H, D = q.shape
+    if q.stride(-1) != 1 or kv_cache.stride(-1) != 1 or kv_cache.stride(1) != kv_cache.shape[2]:
+        raise ValueError("rows must be contiguous")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise TypeError("block_table and seq_lens must be int32 (seq_lens contiguous)")
+    if block_table.stride(-1) != 1:
+        raise ValueError("block_table rows must be contiguous")
+    if seq_lens.numel() != B or block_table.dim() != 2 or block_table.shape[0] < B:
+        raise ValueError("seq_lens must hold B entries and block_table B rows")
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != D:
+        raise ValueError("kv_cache must be [num_blocks, block_size, R + P]")
+    if kv_scale is not None and kv_scale.numel() < 1:
+        raise ValueError("kv_scale must hold one fp32 value")
+    if o is None:
+        o = torch.empty((B, H, R), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if not (o.is_contiguous() and lse.is_contiguous() and lse.dtype == torch.float32 and o.dtype == q.dtype):
+        raise ValueError("o must be contiguous in q's dtype and lse contiguous fp32")
+    if tuple(o.shape) != (B, H, R) or tuple(lse.shape) != (B, H):
+        raise ValueError("o must be [B, H, R] and lse [B, H]")
     return o, lse
 
 

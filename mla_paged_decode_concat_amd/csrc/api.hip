@@ -43,6 +43,25 @@ int device_lds_per_cu() {
 
 int elem_bytes(int dt) { return dt == MLA_F32 ? 4 : dt == MLA_BF16 ? 2 : 1; }
 
+// Scratch for mla_decode_noalloc: the split partials of one decode.  A
+// __device__ variable exists once per GPU the module is loaded on.  In host
+// code `scratch` only names the variable; its device address on the current
+// GPU comes from hipGetSymbolAddress and is kept per device.
+static __device__ __align__(256) float scratch[MLA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+float* g_scratch[kMaxDevices];   // device address of `scratch` per device; null = not looked up yet
+
+float* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  float* ptr = __atomic_load_n(&g_scratch[dev], __ATOMIC_ACQUIRE);
+  if (ptr) return ptr;
+  void* a = nullptr;
+  if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || a == nullptr) return nullptr;
+  ptr = static_cast<float*>(a);
+  __atomic_store_n(&g_scratch[dev], ptr, __ATOMIC_RELEASE);
+  return ptr;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
@@ -421,6 +440,27 @@ int mla_merge_partials(const void* o_parts, const float* lse_parts, int G, int B
   const hipError_t e = launch_shard_merge(dtype, R, o_parts, lse_parts, G, (long long)B * H, o, lse,
                                           reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_decode_noalloc(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_dtype,
+                       int B, int H,
+                       const void* cache, int cache_dtype, int64_t num_blocks, int block_size,
+                       int64_t block_stride, int kv_lora_rank, int rope_dim,
+                       const int32_t* block_table, int64_t block_table_stride, int max_blocks_per_seq,
+                       const int32_t* seq_lens,
+                       float sm_scale, const float* kv_scale,
+                       int num_kv_splits,
+                       void* o, float* lse, void* stream) {
+  // the size check before the device lookup, so an oversized call fails the
+  // same way on every device; argument errors are left to mla_decode_ex
+  const size_t need = mla_decode_workspace_bytes(B, H, num_kv_splits, kv_lora_rank);
+  if (need > MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_WORKSPACE;
+  float* ws = device_scratch();
+  if (!ws) return MLA_ERR_HIP;
+  return mla_decode_ex(q, q_stride_b, q_stride_h, q_dtype, B, H, cache, cache_dtype, num_blocks, block_size,
+                       block_stride, kv_lora_rank, rope_dim, block_table, block_table_stride, max_blocks_per_seq,
+                       seq_lens, sm_scale, kv_scale, num_kv_splits, ws, MLA_NOALLOC_SCRATCH_BYTES, o, lse, stream,
+                       nullptr);
 }
 
 int mla_decode(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_dtype,

@@ -227,3 +227,16 @@ def test_linear_validation():
     lib = binding.load_library()
     assert lib.mla_linear_workspace_bytes(8, 24, 1536) == 0          # unsupported N
     assert lib.mla_linear_workspace_bytes(0, 256, 1536) == 0
+
+
+def test_decode_noalloc_rejects_sizes_beyond_its_scratch():
+    """mla_decode_noalloc checks the workspace the call needs against its
+    fixed scratch size before anything else (no device is touched)."""
+    lib = binding.load_library()
+    v, i = ctypes.c_void_p, ctypes
+    args = [FAKE, 128 * 576, 576, 1, 64, 128, FAKE, 1, 9000, 64, 64 * 576, 512, 64, FAKE, 128, 128, FAKE,
+            ctypes.c_float(0.07), None, 16, FAKE, FAKE, None]
+    # 64 * 128 * 16 * 513 * 4 bytes = 269 MB > 64 MiB
+    assert lib.mla_decode_noalloc(*args) == -3
+    args[19] = 64                    # still more than the scratch holds
+    assert lib.mla_decode_noalloc(*args) == -3
