@@ -124,6 +124,7 @@ def parse():
     ap.add_argument("--heads-per-group", type=int, default=0)
     ap.add_argument("--partition", type=int, default=0)
     ap.add_argument("--no-invariant", action="store_true", help="skip the num_kv_splits=1 timing")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload runs")
     ap.add_argument("--main-only", action="store_true",
                     help="run only the warmup and timed step loop (profiler runs: every decode launch is a step's)")
     return ap.parse_args()
@@ -337,6 +338,12 @@ def main():
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(bt, step_kv_c, step_k_pe, step_slots, args.cpu_seconds)
 
+    configs = None
+    if not (args.main_only or args.no_configs):
+        del ws, o, lse
+        torch.cuda.empty_cache()
+        configs = config_runs(M, W, torch, dev, cus, min(3.0, args.cpu_seconds))
+
     out = {
         "metric": METRIC,
         "value": round(ms_per_step * 1e3, 2),
@@ -358,6 +365,8 @@ def main():
             "seq_len": 8192,
             "num_heads": H,
             "num_kv_splits": S,
+            "partition": "balanced",
+            "partials_per_request": effective_splits(bt.seq_lens_list, S, cus),
             "parallelism": "single GPU",
         },
         "roofline": {
@@ -383,9 +392,97 @@ def main():
         "decode_us_llc_flushed_p10_p50_p90": [round(pct(fl_us, q), 2) for q in (10, 50, 90)] if fl_us else None,
         "num_kv_splits_effective": effective_splits(bt.seq_lens_list, S, cus),
         "beyond_single_token": extras,
+        "configs": configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+# binding roofline per workload (algorithmic bytes vs flops at the spec peaks):
+# an fp8 cache keeps q in bf16, so its contractions run on bf16 matrix cores
+# and its arithmetic intensity (~484 flop/B of KV) is past the bf16 ridge
+BINDING = {0: "hbm", 1: "hbm", 2: "hbm", 3: "hbm", 4: "mfma"}
+
+
+def config_runs(M, W, torch, dev, cus, cpu_seconds):
+    """Every workload at full size in the benchmark's launch configuration
+    (num_kv_splits from the library's rule, default kernel and partition),
+    plus the V3 shape under the pages' literal partition at S = 16.  Each
+    entry: stage times (HIP events on the launch stream, median of 20
+    decodes after 5 untimed ones), KV-read GB/s and MFMA TFLOP/s of the
+    decode, the binding roofline's fraction, and the oracle on a bounded
+    sample of the same batch."""
+    out = {}
+    runs = [(0, {}), (1, {}), (2, {}), (2, {"partition": 1}), (3, {}), (4, {})]
+    for index, kw in runs:
+        spec = W.SPECS[index]
+        bt = W.make_batch(index, dev, pad_table_with_spare=False)
+        M.cache_write(bt.kv_c, bt.k_pe, bt.cache, bt.slot_mapping, "fp8" if spec.cache_dtype == "fp8" else "auto",
+                      bt.scale)
+        N = sum(bt.seq_lens_list)
+        S = M.num_kv_splits(max(bt.seq_lens_list), cus)
+        ws = torch.empty(max(1, M.decode_workspace_bytes(bt.B, bt.H, S, spec.R) // 4), dtype=torch.float32,
+                         device=dev)
+
+        def dec(evs=None):
+            return M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, W.SM_SCALE, S, spec.R, kv_scale=bt.scale,
+                            workspace=ws, stage_events=evs, **kw)
+        for _ in range(5):
+            dec()
+        evs = [[HipEvent() for _ in range(3)] for _ in range(20)]
+        for e in evs:
+            dec(e)
+        torch.cuda.synchronize()
+        s1 = statistics.median(e[0].ms_until(e[1]) * 1e3 for e in evs)
+        s2 = statistics.median(e[1].ms_until(e[2]) * 1e3 for e in evs)
+        tot = statistics.median(e[0].ms_until(e[2]) * 1e3 for e in evs)
+        kv_b = N * spec.D * {"f32": 4, "bf16": 2, "fp8": 1}[spec.cache_dtype]
+        flops = 2.0 * bt.H * (spec.D + spec.R) * N
+        kv_gbps = kv_b / (tot * 1e-6) / 1e9
+        tflops = flops / (tot * 1e-6) / 1e12
+        bound = BINDING[index]
+        frac = kv_gbps / HBM_PEAK_GBS if bound == "hbm" else tflops / BF16_PEAK_TFLOPS
+        name = spec.name + ("_literal_S" + str(S) if kw.get("partition") == 1 else "")
+        entry = {
+            "B": bt.B, "H": bt.H, "R": spec.R, "cache": spec.cache_dtype, "tokens": N, "num_kv_splits": S,
+            "partition": "literal" if kw.get("partition") == 1 or S == 1 else "balanced",
+            "partials_per_request_max": S if kw.get("partition") == 1 else effective_splits(bt.seq_lens_list, S, cus),
+            "stage1_us": round(s1, 2), "stage2_us": round(s2, 2), "decode_us": round(tot, 2),
+            "kv_read_gbps": round(kv_gbps, 1), "mfma_tflops": round(tflops, 1),
+            "roofline": {"bound": bound, "frac": round(frac, 4)},
+        }
+        if cpu_seconds > 0 and not kw:
+            entry["cpu_oracle"] = cpu_decode_sample(bt, cpu_seconds)
+        out[name] = entry
+        del bt, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_decode_sample(bt, seconds):
+    """The oracle's fp64 decode of as many requests of the batch as fit in
+    `seconds` (from the GPU-written cache copied back), scaled to the batch."""
+    from mla_paged_decode_concat_amd import workloads as W
+    from oracle import mla_oracle as O
+    from threadpoolctl import threadpool_info
+    spec = bt.spec
+    cache = W.bits(bt.cache)
+    q = W.bits(bt.q)
+    table = bt.block_table.cpu().numpy()
+    lens = bt.seq_lens.cpu().numpy()
+    scale = float(bt.scale[0].cpu()) if bt.scale is not None else None
+    t0 = time.perf_counter()
+    done = 0
+    for b in range(bt.B):
+        O.decode(q[b:b + 1], cache, table[b:b + 1], lens[b:b + 1], W.SM_SCALE, spec.in_dtype, spec.cache_dtype,
+                 spec.R, scale)
+        done += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    el = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(el / done * bt.B * 1e6, 1), "unit": "us/decode", "cores": int(threads),
+            "sample": f"{done} of {bt.B} requests, scaled"}
 
 
 def pct(sorted_vals, q):

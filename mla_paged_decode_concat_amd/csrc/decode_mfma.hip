@@ -1021,10 +1021,11 @@ struct Stage1AB {
               pf[nb] = *MLA_LDS(const bf16x8_t, pbuf(smem, k - 1, hg) + nb * 1024 + lane * 16);
             pv<CBB, CA, kVRingB>(acc, vslot(smem, k - 1), pf);
           }
-          // Tile k+2 after this wave's PV: by now tile k+1 has mostly
-          // landed, so the issue does not stall on a full load queue (issued
-          // first, it held the PV back by about a thousand cycles), and it
-          // still has about one and a half intervals to land.
+          // Tile k+2 once this wave's PV is issued: tile k+1 has mostly
+          // landed by then, so the issue rarely stalls on a full load queue,
+          // and it still has about one and a half intervals to land.  (Issued
+          // before the PV, or one instruction at a time spread over the PV,
+          // the decode time is the same within noise.)
           if (k + 2 < T) issue<NT>(p, sa, k + 2, se, pg0, smem, s_table, hg);
         }
       }
