@@ -1079,6 +1079,387 @@ struct Stage1AB {
   }
 };
 
+// The two-role stage 1 of Stage1AB for a 128-head group on an fp8 (E4M3)
+// cache.  Tiles keep the fp8 layout of TileLoad8 (value columns as 8-token x
+// 128-byte blocks, the 64 rope bytes of a token as half blocks), in a 4-slot
+// ring for the value columns and a 3-slot ring for the rope columns.  The
+// matrix cores read K and V^T from the fp8 tile and convert them to bf16 in
+// registers (exact).  P reaches the PV wave as bf16 plus its bf16 rounding
+// remainder, the second operand of a second MFMA per V^T fragment, as in
+// Stage1's fp8 path; kv_scale scales the scores and the output.  Same
+// accumulation order as Stage1's fp8 path: the same bits.
+template <int R, int CA>
+struct Stage1AB8 {
+  using G = Geo<R>;
+  using TL8 = TileLoad8<R, 4>;
+  static constexpr int NW_ = 8;
+  static constexpr int HPG = 128;
+  static constexpr int CB = G::CB;
+  static constexpr int CBB = CB - CA;
+  static_assert(CA >= 1 && CBB >= 1, "column split");
+  static constexpr int FG = R / 128;               // full 128-byte column groups (values)
+  static constexpr int LPW = FG + 1;               // load instructions per PV wave per tile
+  static constexpr int KP = G::KS / 2;             // QK k-step pairs
+  static constexpr int VP = R / 64;                // pairs over the value columns
+  static constexpr int VSLOT = FG * 4096;
+  static constexpr int RSLOT = 4 * 512;
+  static constexpr int NV = 4, NR = 3;
+  static constexpr int P_OFF = NV * VSLOT + NR * RSLOT;
+  static constexpr int PBUF = 2 * HPG * kTile * 2;  // P and its remainder, bf16
+  static constexpr int SMEM = P_OFF + 2 * PBUF;
+  static constexpr int TABLE = kTableWindow;
+  static_assert(SMEM + TABLE * 4 + 8 <= 160 * 1024, "LDS");
+
+  static __device__ __forceinline__ char* vslot(char* smem, int t) { return smem + (t % NV) * VSLOT; }
+  static __device__ __forceinline__ char* rslot(char* smem, int t) { return smem + NV * VSLOT + (t % NR) * RSLOT; }
+  // per SIMD: P (2 KB) then its remainder (2 KB)
+  static __device__ __forceinline__ char* pbuf(char* smem, int t, int hg) {
+    return smem + P_OFF + (t & 1) * PBUF + hg * 4096;
+  }
+
+  template <bool NT>
+  static __device__ __forceinline__ void issue(const DecodeParams& p, int sa, int t, int se, int pg0, char* smem,
+                                               const int* s_table, int hg) {
+    const int lane = lane_now();
+    const typename TL8::Rows rw = TL8::rows(p, sa + kTile * t, se, pg0, s_table, hg);
+    char* vb = vslot(smem, t);
+    char* rb = rslot(smem, t);
+    static_for<FG>([&](auto K) {
+      constexpr int k = decltype(K)::value;
+      dma16<128 * k, NT>(rw.full[0], lds_addr(vb) + (4 * k + hg) * 1024);
+    });
+    if (lane < 32) dma16<0, NT>(rw.rope[0], lds_addr(rb) + hg * 512);
+  }
+
+  template <bool NT>
+  static __device__ void piece(const DecodeParams& p, int b, int a, int e, int part, int head0,
+                               char* smem, int* s_table, int* s_flags) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (wave < 4) run<true, NT>(p, b, a, e, part, head0, wave, smem, s_table, s_flags);
+    else run<false, NT>(p, b, a, e, part, head0, wave - 4, smem, s_table, s_flags);
+  }
+
+  // V^T fragments from the fp8 tile: in lane group g, source lane
+  // r16 = 2i + hh names the token bound to k-slot i and byte half hh of a
+  // 16-column block (8-bit transpose read).  The lane's part of the address
+  // is worked out once per tile (base and the token's swizzle key); a column
+  // block adds an immediate and one xor.
+  struct VLane {
+    uint32_t base;   // LDS address of the lane's token row in column group 0, plus its byte half
+    int t8v;         // swizzle key of that row
+  };
+  static __device__ __forceinline__ VLane vlane(const char* vt) {
+    const int lane = lane_now();
+    const int g = lane >> 4, r16 = lane & 15;
+    const int i8 = r16 >> 1, hh = r16 & 1;
+    const int tok = i8 < 4 ? 4 * g + i8 : 12 + 4 * g + i8;
+    const int tqv = tok >> 3, t8v = tok & 7;
+    return VLane{lds_addr(vt) + (uint32_t)(tqv * 1024 + 8 * t8v * 16 + 8 * hh), t8v};
+  }
+  static __device__ __forceinline__ v2i32_t vread8(const VLane& vl, int cb) {
+    const uint32_t a = vl.base + (uint32_t)((cb >> 3) * 4096) + (uint32_t)(((cb & 7) ^ vl.t8v) * 16);
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(MLA_LDS(v2i32_t, (uintptr_t)a));
+  }
+
+  // O^T += V^T (P + remainder)^T over column blocks CB0 .. CB0+N-1, two
+  // column blocks at a time: the four products against P, then the four
+  // against its remainder, so that each accumulator's second update is four
+  // MFMAs behind its first instead of waiting on it back to back (every
+  // accumulator still adds P's term, then the remainder's).  V^T fragments
+  // go through a 4-slot ring: the current pair and the next pair in flight.
+  template <int N, int CB0>
+  static __device__ __forceinline__ void pv(f32x4_t (&acc)[N][2], const char* vt, const bf16x8_t (&pf)[2],
+                                            const bf16x8_t (&pl)[2]) {
+    const VLane vl = vlane(vt);
+    __builtin_amdgcn_sched_barrier(0);
+    v2i32_t vw[4];
+    vw[0] = vread8(vl, CB0);
+    if (N > 1) vw[1] = vread8(vl, CB0 + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<(N + 1) / 2>([&](auto CI) {
+      constexpr int c = 2 * decltype(CI)::value;
+      constexpr bool two = c + 1 < N;
+      if (c + 2 < N) vw[(c + 2) % 4] = vread8(vl, CB0 + c + 2);
+      if (c + 3 < N) vw[(c + 3) % 4] = vread8(vl, CB0 + c + 3);
+      const bf16x8_t vf0 = fp8x8_to_bf16((uint32_t)vw[c % 4][0], (uint32_t)vw[c % 4][1]);
+      bf16x8_t vf1 = vf0;
+      if constexpr (two) vf1 = fp8x8_to_bf16((uint32_t)vw[(c + 1) % 4][0], (uint32_t)vw[(c + 1) % 4][1]);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[c][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf0, pf[nb], acc[c][nb], 0, 0, 0);
+      if constexpr (two) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[c + 1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf1, pf[nb], acc[c + 1][nb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[c][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf0, pl[nb], acc[c][nb], 0, 0, 0);
+      if constexpr (two) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[c + 1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf1, pl[nb], acc[c + 1][nb], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+
+  // QK wave, one tile
+  static __device__ __forceinline__ void qk_tile(const bf16x8_t (&qf)[2][G::KS], f32x4_t (&acc)[CA][2],
+                                                 float (&m_ref)[2], float (&l_sum)[2], float (&l_mma)[2],
+                                                 float (&m_init)[2], const char* vt, const char* rt, char* pb,
+                                                 int tile_start, int se, float c2, int* flag) {
+    const int lane = lane_now();
+    const int g = lane >> 4, r16 = lane & 15;
+    const int t8 = r16 & 7;
+    // K fragments straight from the fp8 tile: for k-step pair kp and token
+    // block mb, lane (token r16, group g) reads the 16 bytes of dims
+    // 64kp + 16g .. +16 and converts them to the bf16 fragments of k-steps
+    // 2kp and 2kp + 1 (Q's fragments are loaded in the same order)
+    // the lane's part of the K addresses, once per tile: value rows of the
+    // two k-step parities (the block and token-block parts are immediates)
+    // and the rope row
+    const uint32_t kv0 = lds_addr(vt) + (uint32_t)((r16 >> 3) * 1024 + (8 * t8 + (g ^ t8)) * 16);
+    const uint32_t kv1 = lds_addr(vt) + (uint32_t)((r16 >> 3) * 1024 + (8 * t8 + ((4 + g) ^ t8)) * 16);
+    const uint32_t krp = lds_addr(rt) + (uint32_t)((r16 >> 3) * 512 + (4 * t8 + ((g + (t8 >> 1)) & 3)) * 16);
+    auto kread = [&](int kp, int mb) -> u32x4_t {
+      const uint32_t ad = kp < VP ? ((kp & 1) ? kv1 : kv0) + (uint32_t)((4 * (kp >> 1) + 2 * mb) * 1024)
+                                  : krp + (uint32_t)(2 * mb * 512);
+      return *MLA_LDS(const u32x4_t, (uintptr_t)ad);
+    };
+    f32x4_t s[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) s[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    u32x4_t kw[2][2];
+    kw[0][0] = kread(0, 0);
+    kw[0][1] = kread(0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kp = 0; kp < KP; ++kp) {
+      if (kp + 1 < KP) {
+        kw[(kp + 1) & 1][0] = kread(kp + 1, 0);
+        kw[(kp + 1) & 1][1] = kread(kp + 1, 1);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const u32x4_t w = kw[kp & 1][mb];
+        const bf16x8_t k0 = fp8x8_to_bf16(w[0], w[1]);
+        const bf16x8_t k1 = fp8x8_to_bf16(w[2], w[3]);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          s[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[nb][2 * kp], s[mb][nb], 0, 0, 0);
+          s[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[nb][2 * kp + 1], s[mb][nb], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    bool need = false;
+    float mt[2];
+    const bool full = tile_start + kTile <= se;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      mt[nb] = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = tile_start + 16 * mb + 4 * g + i;
+          const float v = full || tok < se ? s[mb][nb][i] * c2 : -INFINITY;
+          s[mb][nb][i] = v;
+          mt[nb] = fmaxf(mt[nb], v);
+        }
+      need |= mt[nb] > m_ref[nb] + kSlack;
+    }
+    if (__builtin_expect(__any(need), 0)) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float m = mt[nb];
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        if (m_ref[nb] == -INFINITY) {
+          m_ref[nb] = m;
+        } else if (m > m_ref[nb] + kSlack) {
+          m_init[nb] = m;
+          *flag = 1;
+        }
+      }
+    }
+    // P in bf16 and its bf16 rounding remainder (the value columns are then
+    // summed against p to ~16 significant bits)
+    bf16x8_t pf[2], pl[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float ls = 0.0f, lm = 0.0f;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pj = __builtin_amdgcn_exp2f(s[mb][nb][i] - m_ref[nb]);
+          const __bf16 pb = (__bf16)pj;
+          const __bf16 pr = (__bf16)(pj - (float)pb);
+          ls += pj;
+          pf[nb][4 * mb + i] = pb;
+          pl[nb][4 * mb + i] = pr;
+          lm += (float)pb + (float)pr;
+        }
+      l_sum[nb] += ls;
+      l_mma[nb] += lm;
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      *MLA_LDS(bf16x8_t, pb + nb * 1024 + lane * 16) = pf[nb];
+      *MLA_LDS(bf16x8_t, pb + 2048 + nb * 1024 + lane * 16) = pl[nb];
+    }
+    pv<CA, 0>(acc, vt, pf, pl);
+  }
+
+  template <bool QKW, bool NT>
+  static __device__ __forceinline__ void run(const DecodeParams& p, int b, int a, int e, int part, int head0, int hg,
+                                             char* smem, int* s_table, int* s_flags) {
+    const int hb = head0 + 32 * hg;
+    constexpr int NACC = QKW ? CA : CBB;
+    constexpr int CB0 = QKW ? 0 : CA;
+    const float kvs = *p.kv_scale;
+
+    // Q^T operand (QK wave), in the fp8 path's order: k-step pair kp = ks / 2
+    // covers dims 64kp .. +64, of which lane group g takes 64kp + 16g .. +16,
+    // half ks % 2 in k-step ks
+    bf16x8_t qf[2][G::KS];
+    if constexpr (QKW) {
+      const int lane = threadIdx.x & 63;
+      const int g = lane >> 4;
+      const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + (long long)b * p.q_sb;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int h = hb + 16 * nb + (lane & 15);
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks)
+          qf[nb][ks] = *reinterpret_cast<const bf16x8_t*>(qb + (long long)h * p.q_sh + 64 * (ks >> 1) + 16 * g +
+                                                          8 * (ks & 1));
+      }
+      wait_vmcnt<0>();
+    }
+
+    f32x4_t acc[NACC][2];
+    float m_ref[2], l_sum[2], l_mma[2], m_init[2] = {-INFINITY, -INFINITY};
+    const float c2 = p.sm_scale * kvs * kLog2e;
+    auto reset = [&]() {
+#pragma unroll
+      for (int c = 0; c < NACC; ++c)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[c][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        m_ref[nb] = m_init[nb];
+        l_sum[nb] = 0.0f;
+        l_mma[nb] = 0.0f;
+      }
+    };
+    reset();
+
+    const int bs = p.block_size;
+    const int32_t* btab = p.block_table + (long long)b * p.bt_stride;
+#pragma unroll 1
+    for (int sa = a; sa < e;) {
+      const int pg0 = sa / bs;
+      const long long win_end = (long long)(pg0 + TABLE) * bs;
+      int se = e;
+      if (win_end < e) se = sa + (int)((win_end - sa) / kTile) * kTile;
+      __syncthreads();
+      const int npg = (se - 1) / bs - pg0 + 1;
+      for (int i = threadIdx.x; i < npg; i += NW_ * 64) s_table[i] = btab[pg0 + i];
+      if (threadIdx.x == 0) {
+        s_flags[0] = 0;
+        s_flags[1] = 0;
+      }
+      __syncthreads();
+
+      const int T = (se - sa + kTile - 1) / kTile;
+      wait_vmcnt<0>();   // see Stage1AB: no load of this wave is in flight here
+      if constexpr (!QKW) {
+        issue<NT>(p, sa, 0, se, pg0, smem, s_table, hg);
+        if (T > 1) issue<NT>(p, sa, 1, se, pg0, smem, s_table, hg);
+      }
+      bool redo = false;
+#pragma unroll 1
+      for (int k = 0; k <= T; ++k) {
+        if constexpr (!QKW) {
+          if (k + 1 < T) wait_vmcnt<LPW>();
+          else wait_vmcnt<0>();
+        }
+        __syncthreads();
+        if (k > 0 && s_flags[(k - 1) & 1]) {
+          redo = true;
+          break;
+        }
+        if constexpr (QKW) {
+          if (k < T)
+            qk_tile(qf, acc, m_ref, l_sum, l_mma, m_init, vslot(smem, k), rslot(smem, k), pbuf(smem, k, hg),
+                    sa + kTile * k, se, c2, &s_flags[k & 1]);
+        } else {
+          if (k >= 1) {
+            const int lane = lane_now();
+            bf16x8_t pf[2], pl[2];
+            const char* pbk = pbuf(smem, k - 1, hg);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+              pf[nb] = *MLA_LDS(const bf16x8_t, pbk + nb * 1024 + lane * 16);
+              pl[nb] = *MLA_LDS(const bf16x8_t, pbk + 2048 + nb * 1024 + lane * 16);
+            }
+            pv<CBB, CA>(acc, vslot(smem, k - 1), pf, pl);
+          }
+          if (k + 2 < T) issue<NT>(p, sa, k + 2, se, pg0, smem, s_table, hg);
+        }
+      }
+      wait_vmcnt<0>();
+      if (redo) {
+        reset();
+        sa = a;
+      } else {
+        sa = se;
+      }
+    }
+
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, r16 = lane & 15;
+    __syncthreads();
+    float* s_inv = reinterpret_cast<float*>(smem);
+    float inv[2];
+    if constexpr (QKW) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float l = l_sum[nb], lm = l_mma[nb];
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        lm += __shfl_xor(lm, 16, 64);
+        lm += __shfl_xor(lm, 32, 64);
+        inv[nb] = kvs / lm;
+        if (g == 0) {
+          s_inv[hg * 32 + 16 * nb + r16] = inv[nb];
+          store_partial_lse(p, b, part, hb + 16 * nb + r16, R, (m_ref[nb] + __builtin_amdgcn_logf(l)) * kLn2);
+        }
+      }
+    }
+    __syncthreads();
+    if constexpr (!QKW) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) inv[nb] = s_inv[hg * 32 + 16 * nb + r16];
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int h = hb + 16 * nb + r16;
+#pragma unroll
+      for (int c = 0; c < NACC; ++c) {
+        const f32x4_t v = acc[c][nb] * inv[nb];
+        if (p.direct) store_partial4<true>(p, b, part, h, R, 16 * (CB0 + c) + 4 * g, v[0], v[1], v[2], v[3]);
+        else store_partial4<false>(p, b, part, h, R, 16 * (CB0 + c) + 4 * g, v[0], v[1], v[2], v[3]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+};
+
 // Token-split stage 1 for one group of 16 * NB heads (bf16 cache).  When
 // the token ranges are few (the partial-slot cap binds, or the literal
 // partition has fewer items than CUs), a workgroup whose waves share each
@@ -1491,8 +1872,10 @@ constexpr int lds_bytes() { return K::SMEM + K::TABLE * (int)sizeof(int) + 2 * (
 // the 128-head kernel for an R = 512 bf16 cache, and its column split
 template <int R, bool F8>
 struct Wide {
-  static constexpr bool AB = R == 512 && !F8;
-  using K = typename std::conditional<AB, Stage1AB<R, 5, 2, 2, 2>, Stage1<R, 2, 4, stages_for<R, 4, F8>(), F8>>::type;
+  using K = typename std::conditional<
+      R == 512,
+      typename std::conditional<F8, Stage1AB8<R, 5>, Stage1AB<R, 5, 2, 2, 2>>::type,
+      Stage1<R, 2, 4, stages_for<R, 4, F8>(), F8>>::type;
 };
 
 template <int R, bool F8>
