@@ -127,6 +127,10 @@ def parse():
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload runs")
     ap.add_argument("--main-only", action="store_true",
                     help="run only the warmup and timed step loop (profiler runs: every decode launch is a step's)")
+    ap.add_argument("--num-kv-splits", type=int, default=0,
+                    help="splits per request in the step loop (0 = the library's rule; 1 = the batch-invariant step)")
+    ap.add_argument("--configs-only", action="store_true",
+                    help="run only the per-workload runs (profiler runs: one bulk cache write opens each workload)")
     return ap.parse_args()
 
 
@@ -144,12 +148,17 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     M.load_library()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    if args.configs_only:
+        configs = config_runs(M, W, torch, dev, cus, min(3.0, args.cpu_seconds))
+        copy_probe(torch, dev, args.copy_probe_mb)
+        print(json.dumps({"configs": configs}), flush=True)
+        return
     spec = W.SPECS[2]
     bt = W.make_batch(2, dev, pad_table_with_spare=False)
     B, H, R, D = bt.B, spec.H, spec.R, spec.D
     N = sum(bt.seq_lens_list)
-    cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    S = M.num_kv_splits(max(bt.seq_lens_list), cus)
+    S = args.num_kv_splits or M.num_kv_splits(max(bt.seq_lens_list), cus)
 
     # bulk write of the whole context (reported separately)
     ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -318,12 +327,7 @@ def main():
             "linear_o_absorbed_gbps": round(lin["o_absorbed"][1] / (lin["o_absorbed"][0] * 1e-6) / 1e9, 1),
         }
 
-    if args.copy_probe_mb:
-        src = torch.empty(args.copy_probe_mb * (1 << 20) // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
+    copy_probe(torch, dev, args.copy_probe_mb)
 
     # algorithmic bytes and flops of one stage-1 launch
     kv_bytes = N * D * 2
@@ -365,7 +369,7 @@ def main():
             "seq_len": 8192,
             "num_heads": H,
             "num_kv_splits": S,
-            "partition": "balanced",
+            "partition": "balanced" if S > 1 else "one split per request",
             "partials_per_request": effective_splits(bt.seq_lens_list, S, cus),
             "parallelism": "single GPU",
         },
@@ -409,7 +413,7 @@ def config_runs(M, W, torch, dev, cus, cpu_seconds):
     (num_kv_splits from the library's rule, default kernel and partition),
     plus the V3 shape under the pages' literal partition at S = 16.  Each
     entry: stage times (HIP events on the launch stream, median of 20
-    decodes after 5 untimed ones), KV-read GB/s and MFMA TFLOP/s of the
+    decodes after about 40 ms of untimed ones), KV-read GB/s and MFMA TFLOP/s of the
     decode, the binding roofline's fraction, and the oracle on a bounded
     sample of the same batch."""
     out = {}
@@ -427,7 +431,16 @@ def config_runs(M, W, torch, dev, cus, cpu_seconds):
         def dec(evs=None):
             return M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, W.SM_SCALE, S, spec.R, kv_scale=bt.scale,
                             workspace=ws, stage_events=evs, **kw)
+        # untimed calls for about 40 ms of GPU time: the board's clocks
+        # settle over the first tens of milliseconds of load (a V3-shape
+        # decode measured 201 us after 5 untimed calls, 164 us after 100)
         for _ in range(5):
+            dec()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        dec()
+        torch.cuda.synchronize()
+        for _ in range(min(400, int(0.04 / max(time.perf_counter() - t0, 1e-5)))):
             dec()
         evs = [[HipEvent() for _ in range(3)] for _ in range(20)]
         for e in evs:
@@ -457,6 +470,18 @@ def config_runs(M, W, torch, dev, cus, cpu_seconds):
         del bt, ws
         torch.cuda.empty_cache()
     return out
+
+
+def copy_probe(torch, dev, mb):
+    """One plain device copy of `mb` MiB: its FETCH_SIZE and WRITE_SIZE
+    readings calibrate the counters against bytes known to move."""
+    if not mb:
+        return
+    src = torch.empty(mb * (1 << 20) // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def cpu_decode_sample(bt, seconds):
