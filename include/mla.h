@@ -68,11 +68,11 @@ int mla_num_kv_splits(int64_t max_seq_len, int num_cus, int batch_invariant);
 
 /*
  * Bytes of the fp32 split workspace: B * H * num_kv_splits * (kv_lora_rank + 1)
- * values, the size of the pages' [B, H, num_kv_splits, kv_lora_rank + 1]
- * workspace, holding per (request, head, split) the normalised partial output
- * and its natural-log LSE.  This library uses it as a pool of
- * B * num_kv_splits partial slots per head: partial rows
- * [H, B * num_kv_splits, kv_lora_rank] followed by the LSEs
+ * values.  Only this size follows the pages (their workspace is
+ * [B, H, num_kv_splits, kv_lora_rank + 1]: per request, head and split the
+ * normalised partial output and its LSE).  The layout is this library's own
+ * and internal: a pool of B * num_kv_splits partial slots per head, partial
+ * rows [H, B * num_kv_splits, kv_lora_rank] followed by the natural-log LSEs
  * [H, B * num_kv_splits], so that every row starts on a cache line.
  * [ESSAY: Data flow (attn_logits shape, the "+1" LSE slot);
  * API: _reserve_attn_logits_workspace sizes it once at the worst case]
@@ -240,7 +240,10 @@ int mla_linear_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, int 
  * num_kv_splits sets the workspace size: B * num_kv_splits partials.  With
  * num_kv_splits == 1 every request is one partial, reduced in a fixed order
  * independent of the rest of the batch (batch-invariant mode, [ESSAY: Data
- * flow]).  With num_kv_splits > 1 the library cuts the whole batch into
+ * flow]): the order depends on the request's own length only (for a bf16
+ * cache with H a multiple of 32, requests of MLA_DEFAULT_SPLIT_LEN tokens or
+ * more are cut among four waves of one workgroup; see split_len below), and
+ * stage 1 then writes o and lse itself, with no stage 2.  With num_kv_splits > 1 the library cuts the whole batch into
  * equal token chunks across the GPU's compute units; each piece of a request
  * inside a chunk is one partial, and a long request may take more than
  * num_kv_splits of the B * num_kv_splits slots when shorter requests leave
@@ -302,20 +305,25 @@ int mla_decode(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_dtyp
  *                stage 2, and after stage 2, for timing each stage.
  *   split_len  : batch-invariant decode (num_kv_splits == 1) of a bf16 cache
  *                with H a multiple of 32, under the default kernel, grid and
- *                head grouping: if positive, requests of at least split_len
- *                tokens run the 32-head token-split stage 1 and shorter ones
- *                the stage 1 whose waves share each tile (two launches, each
- *                skipping the other's requests).  The choice depends on the
- *                request's own length only, so a request still decodes to the
- *                same bits in any batch that uses the same split_len.  It pays
+ *                head grouping: requests of at least split_len tokens run the
+ *                32-head token-split stage 1 and shorter ones the stage 1
+ *                whose waves share each tile (two launches, each skipping the
+ *                other's requests).  The choice depends on the request's own
+ *                length only, so a request decodes to the same bits in any
+ *                batch that uses the same split_len.  The token split pays
  *                when the batch's requests are too few to fill the GPU with
  *                shared-tile workgroups and costs when they are many (each
  *                token-split workgroup of 32 heads reads every tile of its
  *                request; the shared-tile one reads it once for up to 128
- *                heads), which a batch-invariant rule cannot see, so it is the
- *                caller's choice.  0 or negative = off (the default).
+ *                heads: about 1.5x for 256 requests of 8192 tokens at
+ *                H = 128), which a batch-invariant rule cannot see.
+ *                0 = MLA_DEFAULT_SPLIT_LEN, negative = off (every request on
+ *                the shared-tile stage 1), positive = that threshold.
  *   reserved   : must be zero.
  */
+/* The length threshold of batch-invariant decode when split_len is 0. */
+#define MLA_DEFAULT_SPLIT_LEN 4096
+
 typedef struct {
   int partition;
   int kernel;

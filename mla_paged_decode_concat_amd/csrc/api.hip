@@ -313,17 +313,23 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
     p.token_split = H % 32 != 0 ? 1 : 0;
   }
   // Batch-invariant decode (one partial per request) with a head count that
-  // 32 divides, if the caller asks for it: a long request can be served by
-  // four waves that each stream a quarter of its tiles for 32 heads (its
-  // 32-head groups re-read each tile from L2) instead of the fill rule's
-  // shared-tile groups, which leave SIMDs idle when the requests are few.
-  // The two kernels sum a request's tiles in different orders, so the choice
-  // is made per request from its own length (in the kernels: each launch
-  // skips the requests of the other), never from the batch.
+  // 32 divides: a long request is served by four waves that each stream a
+  // quarter of its tiles for 32 heads (its 32-head groups re-read each tile
+  // from L2) instead of the fill rule's shared-tile groups, which leave SIMDs
+  // idle when the requests are few.  The two kernels sum a request's tiles in
+  // different orders, so the choice is made per request from its own length
+  // (in the kernels: each launch skips the requests of the other), never from
+  // the batch.  Measured (128 heads, R = 512, bf16): the token split takes
+  // 234 us for 64 requests of 8192 tokens against 490 us, 789 against 1743
+  // for 32 x 32768 and 1528 against 3457 for 16 x 65536, but 906 against
+  // 582 for 256 x 8192, where the shared-tile groups alone fill the GPU;
+  // below 4096 tokens it wins only for small batches (73 against 125 us for
+  // 64 x 2048, 309 against 158 for 256 x 2048).
   int split_len = 0;
+  const int want_split_len = op.split_len == 0 ? MLA_DEFAULT_SPLIT_LEN : op.split_len;
   if (use_mfma && op.kernel == 0 && !op.grid && !op.heads_per_group && cache_dtype == MLA_BF16 &&
-      num_kv_splits == 1 && H % 32 == 0 && op.split_len > 0)
-    split_len = op.split_len;
+      num_kv_splits == 1 && H % 32 == 0 && want_split_len > 0)
+    split_len = want_split_len;
   if (op.grid) {
     p.G = op.grid;
   } else if (p.token_split) {

@@ -5,7 +5,9 @@
 // _fwd_grouped_kernel_stage1): for one request's token range and a group of
 // heads, scores s = sm_scale * q . row over the full R+P row, an online
 // softmax, values = the first R columns of the same rows, and the stored
-// partial (acc / l, m + ln l) in the fp32 workspace [B, H, S, R+1].
+// partial (acc / l, m + ln l) in the fp32 workspace (the pages size it as
+// [B, H, S, R+1]; the slot layout here is this library's own: partial rows
+// [H, slots, R], then the LSEs [H, slots]).
 //
 // How (MI355X-first, not the pages' Triton tiling):
 //  * One workgroup owns a token range and up to 128 heads, so each 32-token

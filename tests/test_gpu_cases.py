@@ -238,31 +238,47 @@ def test_block_permutation_invariance_bit_exact():
             assert torch.equal(oa, ob) and torch.equal(la, lb)
 
 
-def test_batch_invariance_single_split():
+def _alone(bt, b):
+    """Request b of the batch decoded as a batch of one (num_kv_splits = 1)."""
+    o1, l1 = M.decode(bt.q[b:b + 1].contiguous(), bt.cache, bt.block_table[b:b + 1].contiguous(),
+                      bt.seq_lens[b:b + 1].contiguous(), SM, 1, bt.spec.R, kv_scale=bt.scale)
+    torch.cuda.synchronize()
+    return o1[0], l1[0]
+
+
+# 16 heads; 128 heads with requests on both sides of the default token-split
+# threshold; 32 heads of 320-wide rows; 128 heads on an fp8 cache
+INVARIANCE_CASES = [(1, dict(B=6, max_len=3000)), (2, dict(seq_lens=[5000, 4096, 17, 9000, 300, 4095])),
+                    (3, dict(B=6, max_len=6000)), (4, dict(B=6, max_len=6000))]
+
+
+@pytest.mark.parametrize("index,kw", INVARIANCE_CASES)
+def test_batch_invariance_single_split(index, kw):
     """num_kv_splits = 1: a request decodes to the same bits alone and inside
-    a batch."""
-    full = W.make_batch(1, DEV, B=6, max_len=3000)
+    a batch, and the batch matches the oracle."""
+    full = W.make_batch(index, DEV, **kw)
     _write(full)
     o, lse = _decode(full, 1)
-    for b in [0, 3, 5]:
-        o1, l1 = M.decode(full.q[b:b + 1].contiguous(), full.cache, full.block_table[b:b + 1].contiguous(),
-                          full.seq_lens[b:b + 1].contiguous(), SM, 1, 512)
-        torch.cuda.synchronize()
-        assert torch.equal(o1[0], o[b]) and torch.equal(l1[0], lse[b])
+    o_ref, lse_ref = oracle_decode(full, oracle_cache(full), SM)
+    compare(o, lse, o_ref, lse_ref, full.spec.in_dtype)
+    for b in [0, 1, 3, 5]:
+        o1, l1 = _alone(full, b)
+        assert torch.equal(o1, o[b]) and torch.equal(l1, lse[b]), b
 
 
-def test_batch_invariance_single_split_large_batch():
-    """num_kv_splits = 1 with 16 heads and more requests than compute units:
-    the stage-1 kernel choice must not depend on the batch size, so a request
-    decodes to the same bits alone and inside a batch of 300."""
-    full = W.make_batch(1, DEV, seq_lens=[(37 * i) % 400 + 1 for i in range(300)])
+@pytest.mark.parametrize("index,H", [(1, 16), (4, 128)])
+def test_batch_invariance_single_split_large_batch(index, H):
+    """num_kv_splits = 1 with more requests than compute units: the stage-1
+    kernel choice (head grouping) must not depend on the batch size, so a
+    request decodes to the same bits alone and inside a batch of 300
+    (16 heads on a bf16 cache; 128 heads on an fp8 cache, where a batch of
+    300 takes 128-head groups and a batch of one 16-head groups)."""
+    full = W.make_batch(index, DEV, seq_lens=[(37 * i) % 400 + 1 for i in range(300)], H=H)
     _write(full)
     o, lse = _decode(full, 1)
     for b in [0, 7, 150, 299]:
-        o1, l1 = M.decode(full.q[b:b + 1].contiguous(), full.cache, full.block_table[b:b + 1].contiguous(),
-                          full.seq_lens[b:b + 1].contiguous(), SM, 1, 512)
-        torch.cuda.synchronize()
-        assert torch.equal(o1[0], o[b]) and torch.equal(l1[0], lse[b]), b
+        o1, l1 = _alone(full, b)
+        assert torch.equal(o1, o[b]) and torch.equal(l1, lse[b]), b
 
 
 def test_fp8_write_every_bf16_pattern():
@@ -298,11 +314,12 @@ def test_long_request_takes_free_partial_slots(lens, S, grid):
         compare(o, lse, o_ref, lse_ref, "bf16")
 
 
-def test_single_split_result_independent_of_head_grouping():
+@pytest.mark.parametrize("index", [2, 4])
+def test_single_split_result_independent_of_head_grouping(index):
     """With num_kv_splits = 1 the library picks smaller head groups for small
     batches; every head's result must not depend on the grouping, so a
-    request decodes to the same bits in any batch."""
-    bt = W.make_batch(2, DEV, seq_lens=[3000, 17, 900], seed=11)
+    request decodes to the same bits in any batch (bf16 and fp8 caches)."""
+    bt = W.make_batch(index, DEV, seq_lens=[3000, 17, 900], seed=11)
     _write(bt)
     outs = [_decode(bt, 1, kernel=2, heads_per_group=hpg) for hpg in [128, 64, 32, 16]]
     for o, lse in outs[1:]:
@@ -361,8 +378,28 @@ def test_single_split_length_classes(index, H, split_len):
                           bt.seq_lens[b:b + 1].contiguous(), SM, 1, R, split_len=split_len)
         torch.cuda.synchronize()
         assert torch.equal(o1[0], o[b]) and torch.equal(l1[0], lse[b]), b
-    # without a threshold every request takes the shared-tile kernel, which
+    # with the threshold off every request takes the shared-tile kernel, which
     # differs from the token-split one only in rounding
-    o2, l2 = _decode(bt, 1)
+    o2, l2 = _decode(bt, 1, split_len=-1)
     compare(o2, l2, o_ref, lse_ref, "bf16")
     assert torch.equal(o2[1], o[1]) and torch.equal(l2[1], lse[1])   # 599 tokens: shared-tile either way
+
+
+@pytest.mark.parametrize("index,H", [(2, 128), (3, 32)])
+def test_single_split_default_threshold(index, H):
+    """num_kv_splits = 1 with split_len left at 0 is the library's threshold
+    of 4096 tokens: bit for bit the explicit split_len = 4096 run, for a
+    batch with requests on both sides of it (also through the plain entry
+    point, which takes every default)."""
+    lens = [4500, 4096, 4095, 1, 0, 9000, 300]
+    bt = W.make_batch(index, DEV, seq_lens=lens, seed=23, H=H)
+    R = bt.spec.R
+    _write(bt)
+    o_ref, lse_ref = oracle_decode(bt, oracle_cache(bt), SM)
+    o, lse = _decode(bt, 1)
+    compare(o, lse, o_ref, lse_ref, "bf16")
+    o4, l4 = _decode(bt, 1, split_len=4096)
+    assert torch.equal(o, o4) and torch.equal(lse, l4)
+    on, ln = M.decode_noalloc(bt.q, bt.cache, bt.block_table, bt.seq_lens, SM, 1, R)
+    torch.cuda.synchronize()
+    assert torch.equal(o, on) and torch.equal(lse, ln)
