@@ -110,15 +110,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int OFF, bool NT>
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
   static_assert(OFF >= 0 && OFF < 4096, "immediate offset");
+  // M0 (the LDS destination) is an input operand: the compiler writes it
+  // and knows its value; the s_nop separates that write from the load
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base - OFF);
   if constexpr (NT)
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2 nt" ::"v"(gptr), "s"(m0),
-                 "i"(OFF)
-                 : "memory", "m0");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2 nt" ::"v"(gptr), "{m0}"(m0), "i"(OFF)
+                 : "memory");
   else
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2" ::"v"(gptr), "s"(m0),
-                 "i"(OFF)
-                 : "memory", "m0");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2" ::"v"(gptr), "{m0}"(m0), "i"(OFF)
+                 : "memory");
 }
 
 // This lane's index, read so that the compiler cannot hoist what is derived
