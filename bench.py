@@ -245,26 +245,32 @@ def main():
     # batch-invariant run: one split per request, with the library's default
     # stage 1 (requests of 4096 tokens or more on the token-split kernel), and
     # with that length rule off (every request on the shared-tile kernel)
-    inv_us = inv_off_us = None
+    inv_us = inv_off_us = inv_pieces_us = None
     if not (args.no_invariant or args.main_only):
         ws1 = torch.empty(M.decode_workspace_bytes(B, H, 1, R) // 4, dtype=torch.float32, device=dev)
 
-        def inv_run(split_len):
+        def inv_run(S_, wsx, **kx):
             for _ in range(3):
-                M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, W.SM_SCALE, 1, R, workspace=ws1, o=o, lse=lse,
-                         split_len=split_len, **kw)
+                M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, W.SM_SCALE, S_, R, workspace=wsx, o=o, lse=lse,
+                         **kx)
             torch.cuda.synchronize()
             ta = time.perf_counter()
             n_inv = max(5, K // 5)
             for _ in range(n_inv):
                 M.cache_write(step_kv_c, step_k_pe, bt.cache, step_slots, "auto")
-                M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, W.SM_SCALE, 1, R, workspace=ws1, o=o, lse=lse,
-                         split_len=split_len, **kw)
+                M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, W.SM_SCALE, S_, R, workspace=wsx, o=o, lse=lse,
+                         **kx)
             torch.cuda.synchronize()
             return (time.perf_counter() - ta) * 1e6 / n_inv
 
-        inv_us = inv_run(0)
-        inv_off_us = inv_run(-1)
+        inv_us = inv_run(1, ws1, **kw)
+        inv_off_us = inv_run(1, ws1, split_len=-1, **kw)
+        # fixed pieces of 2048 tokens (partition 3): batch-invariant with four
+        # partials per V3 request; the workspace slots of num_kv_splits = 4
+        S_pc = -(-bt.block_table.shape[1] * spec.block_size // 2048)
+        ws_pc = torch.empty(M.decode_workspace_bytes(B, H, S_pc, R) // 4, dtype=torch.float32, device=dev)
+        inv_pieces_us = inv_run(S_pc, ws_pc, **dict(kw, partition=3, piece_len=2048))
+        del ws_pc
 
     extras = None
     if not args.main_only:
@@ -393,6 +399,7 @@ def main():
         "step_cache_write_us": round(step_write_us, 2),
         "batch_invariant_us_per_step": round(inv_us, 2) if inv_us else None,
         "batch_invariant_shared_tile_only_us_per_step": round(inv_off_us, 2) if inv_off_us else None,
+        "batch_invariant_pieces_2048_us_per_step": round(inv_pieces_us, 2) if inv_pieces_us else None,
         "decode_us_p10_p50_p90": [round(pct(dec_us, q), 2) for q in (10, 50, 90)],
         "decode_us_llc_flushed_p10_p50_p90": [round(pct(fl_us, q), 2) for q in (10, 50, 90)] if fl_us else None,
         "num_kv_splits_effective": effective_splits(bt.seq_lens_list, S, cus),

@@ -291,7 +291,19 @@ int mla_decode(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_dtyp
  *                1 = the pages' literal partition: ceil(n / num_kv_splits)
  *                    tokens per split, empty splits skipped
  *                    [DIFF: triton_decode_attention.py, stage 1 split range],
- *                2 = balanced.
+ *                2 = balanced,
+ *                3 = fixed-length pieces: request b is cut into
+ *                    ceil(n_b / piece_len) pieces of piece_len tokens (the
+ *                    last one shorter), each one partial, merged in piece
+ *                    order.  The reduction order then depends on the
+ *                    request's own length only: a batch-invariant decode
+ *                    that still spreads a long request over several
+ *                    workgroups (the pages' batch-invariant mode is
+ *                    num_kv_splits = 1, one partial per request).  Requires
+ *                    piece_len > 0 and num_kv_splits * piece_len >=
+ *                    max_blocks_per_seq * block_size (MLA_ERR_ARG otherwise);
+ *                    num_kv_splits sizes the workspace only, so a request
+ *                    gives the same bits for any num_kv_splits that fits.
  *   kernel     : 0 = default, 1 = the generic vector-ALU stage 1,
  *                2 = the matrix-core (MFMA) stage 1 (bf16 query only),
  *                3 = the MFMA stage 1 with four waves splitting each token
@@ -319,6 +331,8 @@ int mla_decode(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_dtyp
  *                H = 128), which a batch-invariant rule cannot see.
  *                0 = MLA_DEFAULT_SPLIT_LEN, negative = off (every request on
  *                the shared-tile stage 1), positive = that threshold.
+ *   piece_len  : partition 3 only (and required there): tokens per piece;
+ *                a multiple of 32 keeps pieces on whole 32-token tiles.
  *   reserved   : must be zero.
  */
 /* The length threshold of batch-invariant decode when split_len is 0. */
@@ -331,7 +345,8 @@ typedef struct {
   int heads_per_group;
   void* stage_events[3];
   int split_len;
-  int reserved[3];
+  int piece_len;
+  int reserved[2];
 } mla_decode_opts_t;
 
 /* mla_decode with explicit controls (opts may be NULL = all defaults).

@@ -33,7 +33,7 @@ class MLAError(RuntimeError):
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("partition", ctypes.c_int), ("kernel", ctypes.c_int), ("grid", ctypes.c_int),
                 ("heads_per_group", ctypes.c_int), ("stage_events", ctypes.c_void_p * 3),
-                ("split_len", ctypes.c_int), ("reserved", ctypes.c_int * 3)]
+                ("split_len", ctypes.c_int), ("piece_len", ctypes.c_int), ("reserved", ctypes.c_int * 2)]
 
 
 _lib = None
@@ -213,7 +213,7 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
            kv_scale: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
            o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
            partition: int = 0, kernel: int = 0, grid: int = 0, heads_per_group: int = 0,
-           stage_events=None, split_len: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+           stage_events=None, split_len: int = 0, piece_len: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """MLA decode of q [B, H, R+P] against the paged latent cache.  Returns
     o [B, H, R] (q's dtype) and the natural-log lse [B, H] (fp32).
 
@@ -222,8 +222,10 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
     decode); they run as q_len * H rows of one request, and o and lse come
     back as [B, q_len, H, R] and [B, q_len, H].
 
-    partition, kernel, grid, heads_per_group and split_len are the
-    mla_decode_opts_t controls of include/mla.h (0 = library default);
+    partition, kernel, grid, heads_per_group, split_len and piece_len are
+    the mla_decode_opts_t controls of include/mla.h (0 = library default;
+    partition 3 with piece_len > 0 cuts every request into fixed-length
+    pieces, a batch-invariant split);
     stage_events are three events recorded around the two stages."""
     if isinstance(q, tuple):
         q = torch.cat(q, dim=-1)
@@ -236,7 +238,7 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
         lse_flat = lse.view(B, T * H) if lse is not None else None
         of, lf = decode(flat, kv_cache, block_table, seq_lens, sm_scale, num_kv_splits, kv_lora_rank, kv_scale,
                         workspace, o_flat, lse_flat, partition, kernel, grid, heads_per_group, stage_events,
-                        split_len)
+                        split_len, piece_len)
         return of.view(B, T, H, -1), lf.view(B, T, H)
     B, H, D = q.shape
     R = kv_lora_rank
@@ -249,6 +251,7 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
     _same_gpu(q, kv_cache, block_table, seq_lens, kv_scale, workspace, o, lse)
     opts = DecodeOpts(partition, kernel, grid, heads_per_group)
     opts.split_len = split_len
+    opts.piece_len = piece_len
     if stage_events is not None:   # three torch.cuda.Event (or None) recorded around the two stages
         for i, ev in enumerate(stage_events):
             opts.stage_events[i] = ev.cuda_event if ev is not None else None

@@ -218,8 +218,9 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
   mla_decode_opts_t op;
   memset(&op, 0, sizeof(op));
   if (opts) op = *opts;
-  if (op.partition < 0 || op.partition > 2 || op.kernel < 0 || op.kernel > 3 || op.grid < 0 ||
-      op.heads_per_group < 0 || op.reserved[0] || op.reserved[1] || op.reserved[2])
+  if (op.partition < 0 || op.partition > 3 || op.kernel < 0 || op.kernel > 3 || op.grid < 0 ||
+      op.heads_per_group < 0 || op.piece_len < 0 || (op.partition == 3) != (op.piece_len > 0) || op.reserved[0] ||
+      op.reserved[1])
     return MLA_ERR_ARG;
 
   const bool pair_ok = (q_dtype == MLA_F32 && cache_dtype == MLA_F32) ||
@@ -238,6 +239,11 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
   if (!q || !cache || !block_table || !seq_lens || !workspace || !o || !lse) return MLA_ERR_ARG;
   if (!aligned16(workspace) || !aligned16(o)) return MLA_ERR_ARG;
   if (workspace_bytes < mla_decode_workspace_bytes(B, H, num_kv_splits, kv_lora_rank)) return MLA_ERR_WORKSPACE;
+  // fixed-length pieces: a request of the longest length the table allows
+  // must fit its num_kv_splits partial slots
+  if (op.piece_len > 0 &&
+      (long long)num_kv_splits * op.piece_len < (long long)max_blocks_per_seq * block_size)
+    return MLA_ERR_ARG;
 
   // stage-1 kernel: MFMA for bf16 queries when the geometry allows it
   const bool mfma_ok = q_dtype == MLA_BF16 && mfma_supported(H, kv_lora_rank, cache_dtype) && aligned16(q) &&
@@ -271,8 +277,9 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
   p.H = H;
   p.S = num_kv_splits;
   p.block_size = block_size;
-  if (num_kv_splits == 1 || op.partition == 1) p.partition = PART_LITERAL;
+  if (num_kv_splits == 1 || op.partition == 1 || op.partition == 3) p.partition = PART_LITERAL;
   else p.partition = PART_BALANCED;
+  p.piece_len = op.piece_len;
 
   const int cus = device_cu_count();
   int groups;   // head groups per token chunk

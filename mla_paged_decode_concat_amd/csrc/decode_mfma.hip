@@ -1794,7 +1794,7 @@ __global__ __launch_bounds__(K::NW_ * 64) void stage1_mfma_kernel(DecodeParams p
       const int s = item - b * p.S;
       part = item;                         // slot b * S + s
       const int n = p.seq_lens[b];
-      const int kps = (n + p.S - 1) / p.S;
+      const int kps = literal_piece_tokens(n, p.S, p.piece_len);
       a = s * kps;
       e = min(a + kps, n);
       if (n <= 0 && p.direct && p.len_min <= 0) {

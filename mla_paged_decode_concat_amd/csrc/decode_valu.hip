@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kWave * kValuWaves) void stage1_valu_kernel(DecodeP
     const int s = blockIdx.x - b * p.S;
     const int n = p.seq_lens[b];
     if (n <= 0) return;
-    const int kps = (n + p.S - 1) / p.S;
+    const int kps = literal_piece_tokens(n, p.S, p.piece_len);
     const int a = s * kps;
     const int e = min(a + kps, n);
     if (e <= a) return;
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kWave * kMergeWaves) void stage2_merge_kernel(Decod
   const int h = (blockIdx.x - b * hblocks) * kMergeWaves + wave;
   int k, first;
   if (p.partition == PART_LITERAL) {
-    k = literal_num_partials(p.seq_lens[b], p.S);
+    k = literal_num_partials(p.seq_lens[b], p.S, p.piece_len);
     first = b * p.S;
   } else {
     // The workgroup's waves are heads of one request: wave 0 works out the

@@ -167,9 +167,15 @@ __device__ __forceinline__ int balanced_num_partials(long long start, int n, lon
   return (int)(div_nonneg(start + n - 1, Q) - div_nonneg(start, Q) + 1);
 }
 
-__device__ __forceinline__ int literal_num_partials(int n, int S) {
+// Literal partition: tokens per piece of a request of n tokens, either the
+// pages' ceil(n / S) or a fixed piece length (piece_len > 0, the same for
+// every request whatever the batch), and the number of non-empty pieces.
+__device__ __forceinline__ int literal_piece_tokens(int n, int S, int piece_len) {
+  return piece_len > 0 ? piece_len : (n + S - 1) / S;
+}
+__device__ __forceinline__ int literal_num_partials(int n, int S, int piece_len) {
   if (n <= 0) return 0;
-  const int kps = (n + S - 1) / S;
+  const int kps = literal_piece_tokens(n, S, piece_len);
   return (n + kps - 1) / kps;
 }
 
@@ -220,6 +226,7 @@ struct DecodeParams {
                                    // (bf16) and lse itself and stage 2 is not launched
   int len_min, len_max;            // literal partition: this stage-1 launch takes the requests
                                    // with len_min <= seq_len < len_max
+  int piece_len;                   // literal partition: tokens per piece (0 = ceil(n / S))
 };
 
 // Workspace layout (fp32, B*H*S*(R+1) values as the split workspace of the

@@ -132,6 +132,25 @@ def test_decode_ex_validation():
     assert _decode(O_(0, 3, 0, 16), cache_dt=2, kvs=FAKE) == -2   # ... of a bf16 cache
 
 
+def test_decode_ex_piece_partition_validation():
+    """Fixed-length pieces (partition 3): piece_len is required there and
+    only there, and num_kv_splits pieces of piece_len tokens must cover the
+    longest request the table allows (maxblk 10 x block 64 = 640 tokens)."""
+    O_ = binding.DecodeOpts
+    def opts(partition, piece_len):
+        o = O_(partition, 0, 0, 0)
+        o.piece_len = piece_len
+        return o
+    assert _decode(opts(3, 0)) == -1                           # partition 3 needs a piece length
+    assert _decode(opts(0, 160)) == -1                         # a piece length needs partition 3
+    assert _decode(opts(1, 160)) == -1
+    assert _decode(opts(3, -32)) == -1
+    assert _decode(opts(3, 159)) == -1                         # 4 x 159 < 640
+    assert _decode(opts(3, 64), S=9, wsb=4 * 128 * 9 * 513 * 4) == -1   # 9 x 64 < 640
+    assert _decode(opts(3, 160), B=0) == 0                     # 4 x 160 = 640: valid (empty batch launches nothing)
+    assert _decode(opts(3, 64), S=10, B=0, wsb=4 * 128 * 10 * 513 * 4) == 0
+
+
 def _merge(**kw):
     a = dict(o_parts=FAKE, lse_parts=FAKE, G=4, B=8, H=16, R=512, dt=1, o=FAKE, lse=FAKE, stream=None)
     a.update(kw)

@@ -406,3 +406,41 @@ def test_single_split_default_threshold(index, H):
     on, ln = M.decode_noalloc(bt.q, bt.cache, bt.block_table, bt.seq_lens, SM, 1, R)
     torch.cuda.synchronize()
     assert torch.equal(o, on) and torch.equal(lse, ln)
+
+
+@pytest.mark.parametrize("index,H,piece_len", [(2, 128, 2048), (2, 128, 96), (4, 128, 1024), (3, 32, 512),
+                                               (1, 16, 256), (0, 4, 32)])
+def test_fixed_piece_partition(index, H, piece_len):
+    """Partition 3: every request is cut into ceil(n / piece_len) pieces of
+    piece_len tokens, each one partial, merged in order.  Results match the
+    oracle, and a request gives the same bits alone (with a larger
+    num_kv_splits) as inside the batch: the split depends on its own length
+    only (fp32 on the vector-ALU kernel, 16 heads on the token-split kernel,
+    32 and 128 heads on the shared-tile kernels, bf16 and fp8 caches)."""
+    lens = [5000, 1, 0, piece_len, piece_len + 1, 3 * piece_len - 7, 700]
+    bt = W.make_batch(index, DEV, seq_lens=lens, H=H, seed=31)
+    _write(bt)
+    o_ref, lse_ref = oracle_decode(bt, oracle_cache(bt), SM)
+    max_len = bt.block_table.shape[1] * bt.spec.block_size
+    S = -(-max_len // piece_len)
+    _print(f"[pieces] workload {index} H={H} piece_len={piece_len} S={S}")
+    o, lse = _decode(bt, S, partition=3, piece_len=piece_len)
+    compare(o, lse, o_ref, lse_ref, bt.spec.in_dtype)
+    for b in [0, 1, 2, 4, 5]:
+        o1, l1 = M.decode(bt.q[b:b + 1].contiguous(), bt.cache, bt.block_table[b:b + 1].contiguous(),
+                          bt.seq_lens[b:b + 1].contiguous(), SM, S + 3, bt.spec.R, kv_scale=bt.scale, partition=3,
+                          piece_len=piece_len)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0], o[b]) and torch.equal(l1[0], lse[b]), b
+
+
+def test_fixed_piece_partition_rejects_short_cover():
+    """num_kv_splits pieces of piece_len tokens must cover the table's
+    longest request."""
+    bt = W.make_batch(2, DEV, seq_lens=[1000, 300], H=32)
+    _write(bt)
+    max_len = bt.block_table.shape[1] * bt.spec.block_size
+    with pytest.raises(M.MLAError):
+        _decode(bt, 1, partition=3, piece_len=max_len - 1)
+    o, lse = _decode(bt, 1, partition=3, piece_len=max_len)     # one piece per request: fits
+    assert torch.isfinite(lse).all()

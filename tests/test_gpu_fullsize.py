@@ -7,7 +7,7 @@ checked bit-exactly on sampled tokens against the oracle's write.
 
 Workload 2 (DeepSeek-V3 shape, B=64, H=128, 8192 tokens each) is the one the
 benchmark times; it is also checked with num_kv_splits = 1, the benchmark's
-batch-invariant run.
+batch-invariant run, and with fixed pieces of 2048 tokens (partition 3).
 """
 
 import os
@@ -85,6 +85,11 @@ def test_full_size_default_launch(index):
         torch.cuda.synchronize()
         compare(o1[reqs], lse1[reqs], o_ref, lse_ref, spec.in_dtype)
         _margin_line(index, spec, 1, reqs, margins(o1[reqs], lse1[reqs], o_ref, lse_ref, spec.in_dtype))
+        _print("[full] workload 2: fixed pieces of 2048 tokens, num_kv_splits = 4")
+        o2, lse2 = M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, SM, 4, spec.R, partition=3, piece_len=2048)
+        torch.cuda.synchronize()
+        compare(o2[reqs], lse2[reqs], o_ref, lse_ref, spec.in_dtype)
+        _margin_line(index, spec, 4, reqs, margins(o2[reqs], lse2[reqs], o_ref, lse_ref, spec.in_dtype))
 
 
 def _margin_line(index, spec, S, reqs, m):
