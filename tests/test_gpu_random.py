@@ -3,7 +3,8 @@ count (including counts only the vector kernel takes), lengths (empty, one
 token, ragged, one long request), num_kv_splits, partition and cache type
 drawn per case, and, from a second generator, the stage-1 choice (library
 default, the token-split kernel with 16 or 32 heads, or batch-invariant
-length classes) -- combinations the targeted tests do not enumerate.
+length classes) and from a third whether the batch is cut into fixed-length
+pieces -- combinations the targeted tests do not enumerate.
 MLA_RANDOM_CASES sets the number of cases (100 by default; seeds 42 and 65
 once exceeded the bound on an fp8 cache, before its P carried the bf16
 rounding remainder)."""
@@ -46,6 +47,12 @@ def _case(seed):
     elif mode == "length_classes" and index != 4 and H % 32 == 0:
         S, partition = 1, 0
         opts = dict(split_len=int(r2.choice([1, 300, 1000])))
+    # fixed-length pieces (partition 3), from a third generator; num_kv_splits
+    # is then set from the batch's table width
+    r3 = np.random.default_rng(9000 + seed)
+    if "split_len" not in opts and r3.random() < 0.25:
+        partition = 3
+        opts = dict(opts, piece_len=int(r3.choice([32, 100, 512, 2048])))
     return index, H, lens, S, partition, opts
 
 
@@ -54,6 +61,9 @@ def test_random_configuration_against_oracle(seed):
     index, H, lens, S, partition, opts = _case(seed)
     print(f"[random {seed}] workload {index} H={H} S={S} partition={partition} {opts} lens={lens}", flush=True)
     bt = W.make_batch(index, DEV, seq_lens=lens, H=H, seed=seed)
+    if partition == 3:
+        S = -(-bt.block_table.shape[1] * bt.spec.block_size // opts["piece_len"])
+        print(f"[random {seed}] fixed pieces: num_kv_splits={S}", flush=True)
     ref_cache = oracle_cache(bt)
     M.cache_write(bt.kv_c, bt.k_pe, bt.cache, bt.slot_mapping, "fp8" if bt.spec.cache_dtype == "fp8" else "auto",
                   bt.scale)
