@@ -1794,9 +1794,7 @@ __global__ __launch_bounds__(K::NW_ * 64) void stage1_mfma_kernel(DecodeParams p
       const int s = item - b * p.S;
       part = item;                         // slot b * S + s
       const int n = p.seq_lens[b];
-      const int kps = literal_piece_tokens(n, p.S, p.piece_len);
-      a = s * kps;
-      e = min(a + kps, n);
+      literal_piece_range(n, p.S, p.piece_len, s, a, e);
       if (n <= 0 && p.direct && p.len_min <= 0) {
         // an empty request has no piece: o = 0 and lse = -inf are written
         // here when there is no stage 2 to write them

@@ -134,9 +134,8 @@ __global__ __launch_bounds__(kWave * kValuWaves) void stage1_valu_kernel(DecodeP
     const int s = blockIdx.x - b * p.S;
     const int n = p.seq_lens[b];
     if (n <= 0) return;
-    const int kps = literal_piece_tokens(n, p.S, p.piece_len);
-    const int a = s * kps;
-    const int e = min(a + kps, n);
+    int a, e;
+    literal_piece_range(n, p.S, p.piece_len, s, a, e);
     if (e <= a) return;
     valu_piece<QT, CT, R, P>(p, b, h0, a, e, b * p.S + s, sm_acc, sm_ml);
     return;

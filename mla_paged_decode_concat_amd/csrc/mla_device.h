@@ -175,8 +175,17 @@ __device__ __forceinline__ int literal_piece_tokens(int n, int S, int piece_len)
 }
 __device__ __forceinline__ int literal_num_partials(int n, int S, int piece_len) {
   if (n <= 0) return 0;
-  const int kps = literal_piece_tokens(n, S, piece_len);
-  return (n + kps - 1) / kps;
+  const long long kps = literal_piece_tokens(n, S, piece_len);
+  return (int)(((long long)n + kps - 1) / kps);
+}
+// Token range [a, e) of piece s (empty when it starts past the request),
+// in 64-bit so that no piece index or length overflows.
+__device__ __forceinline__ void literal_piece_range(int n, int S, int piece_len, int s, int& a, int& e) {
+  const long long kps = literal_piece_tokens(n, S, piece_len);
+  const long long a64 = (long long)s * kps;
+  a = a64 < n ? (int)a64 : n;
+  e = (int)(a64 + kps < (long long)n ? a64 + kps : (long long)n);
+  if (e < a) e = a;
 }
 
 // The batch totals and request b's padded start from one pass over
