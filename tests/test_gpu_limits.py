@@ -1,8 +1,9 @@
 """Limits and capture: the split-count cap (num_kv_splits = 2 x CUs for a
 request of a quarter million tokens, every partition and kernel), and the
-whole step -- cache write, decode, shard merge, RoPE, linear layer -- captured
-in a HIP graph and replayed several times with eager work in between, each
-replay equal to the eager result."""
+whole step -- cache write, decode (with a workspace, without allocation, with
+one partial per request and with fixed pieces), shard merge, RoPE, linear
+layer -- captured in a HIP graph and replayed several times with eager work
+in between, each replay equal to the eager result."""
 
 import numpy as np
 import pytest
@@ -61,6 +62,14 @@ def test_graph_capture_and_replay():
     q0 = bt.q.clone()
     qr = bt.q.clone()
     qpos = torch.tensor([n - 1 for n in bt.seq_lens_list], dtype=torch.int64, device=DEV)
+    # the other decode forms: no allocation (library scratch), one partial
+    # per request, fixed pieces of 256 tokens
+    o_na, l_na = torch.empty_like(o), torch.empty_like(lse)
+    ws1 = torch.empty(M.decode_workspace_bytes(bt.B, bt.H, 1, R) // 4, dtype=torch.float32, device=DEV)
+    o1, l1 = torch.empty_like(o), torch.empty_like(lse)
+    S_pc = -(-bt.block_table.shape[1] * bt.spec.block_size // 256)
+    ws_pc = torch.empty(M.decode_workspace_bytes(bt.B, bt.H, S_pc, R) // 4, dtype=torch.float32, device=DEV)
+    o_pc, l_pc = torch.empty_like(o), torch.empty_like(lse)
 
     def step():
         M.cache_write(bt.kv_c, bt.k_pe, bt.cache, bt.slot_mapping, positions=pos, cos_sin_cache=tab)
@@ -69,11 +78,16 @@ def test_graph_capture_and_replay():
         M.decode(qr, bt.cache, bt.block_table, bt.seq_lens, SM, S, R, workspace=ws, o=o, lse=lse)
         M.merge_partials(torch.stack([o, o]), torch.stack([lse, lse]), om, lm)
         M.linear(A, Wt, out=C)
+        M.decode_noalloc(qr, bt.cache, bt.block_table, bt.seq_lens, SM, 2, R, o=o_na, lse=l_na)
+        M.decode(qr, bt.cache, bt.block_table, bt.seq_lens, SM, 1, R, workspace=ws1, o=o1, lse=l1)
+        M.decode(qr, bt.cache, bt.block_table, bt.seq_lens, SM, S_pc, R, workspace=ws_pc, o=o_pc, lse=l_pc,
+                 partition=3, piece_len=256)
 
+    outs = (qr, o, lse, om, lm, C, o_na, l_na, o1, l1, o_pc, l_pc)
     blank = bt.cache.clone()                   # NaN in every slot
     step()
     torch.cuda.synchronize()
-    ref = [t.clone() for t in (bt.cache, qr, o, lse, om, lm, C)]
+    ref = [t.clone() for t in (bt.cache,) + outs]
     graph = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -85,11 +99,11 @@ def test_graph_capture_and_replay():
         step()
     for rep in range(4):
         bt.cache.copy_(blank)                  # eager work that resets or scrambles every output
-        for t in (qr, o, lse, om, lm, C):
+        for t in outs:
             t.view(torch.uint8).fill_(0x55)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for a, b in zip((bt.cache, qr, o, lse, om, lm, C), ref):
-            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}"
+        for i, (a, b) in enumerate(zip((bt.cache,) + outs, ref)):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}, output {i}"
     _print("[limits] 4 replays equal to the eager step")
