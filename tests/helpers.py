@@ -15,6 +15,21 @@ from oracle import mla_oracle as O
 TOL = {"f32": (1e-5, 1e-5), "bf16": (1e-2, 1e-3)}
 
 
+def check_slots(slot_mapping, num_blocks: int, block_size: int) -> None:
+    """Debug validation pass of a cache write's slot mapping (tests only):
+    every non-negative slot lies in [0, num_blocks * block_size) and none
+    repeats.  The write gives each token its own wave with no ordering
+    between them, so a repeated slot would leave whichever row lands last
+    (the library states unique slots as a precondition and does not check
+    device data)."""
+    s = slot_mapping.cpu().numpy() if isinstance(slot_mapping, torch.Tensor) else np.asarray(slot_mapping)
+    real = s[s >= 0]
+    if real.size and int(real.max()) >= num_blocks * block_size:
+        raise ValueError(f"slot {int(real.max())} out of range for {num_blocks} blocks of {block_size}")
+    if np.unique(real).size != real.size:
+        raise ValueError("repeated slot in slot_mapping")
+
+
 def oracle_cache(bt: W.Batch) -> np.ndarray:
     scale = float(bt.scale[0].cpu()) if bt.scale is not None else None
     return O.cache_write(W.bits(bt.cache), W.bits(bt.kv_c), W.bits(bt.k_pe), bt.slot_mapping.cpu().numpy(),

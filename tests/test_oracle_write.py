@@ -68,3 +68,16 @@ def test_fp8_write_matches_torch_cast():
     _check_scatter(cin, out, kv_c, k_pe, slots, enc)
     # scale = amax/448 puts the largest magnitude exactly on 448
     assert (out[np.isin(out, [0x7E, 0xFE])]).size >= 1
+
+
+def test_slot_validation_pass():
+    """The tests' debug validation of a slot mapping: padding (-1) is
+    allowed, a repeated or out-of-range slot is rejected."""
+    import pytest
+    from helpers import check_slots
+    check_slots(np.array([3, -1, 0, 7, -1], dtype=np.int64), 2, 4)
+    with pytest.raises(ValueError):
+        check_slots(np.array([3, -1, 3], dtype=np.int64), 2, 4)
+    with pytest.raises(ValueError):
+        check_slots(np.array([0, 8], dtype=np.int64), 2, 4)
+    check_slots(np.array([], dtype=np.int64), 2, 4)
