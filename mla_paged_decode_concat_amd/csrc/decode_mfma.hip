@@ -198,26 +198,6 @@ struct TileLoad {
     }
     return rw;
   }
-  // the same rows with the page numbers read from the block table in global
-  // memory (btab = the request's row) instead of the staged copy
-  static __device__ __forceinline__ Rows rows_global(const DecodeParams& p, int tile_start, int se,
-                                                     const int32_t* btab, int wave) {
-    const char* cache = reinterpret_cast<const char*>(p.cache);
-    const int lane = lane_now();
-    const int t8 = lane >> 3, x = lane & 7;
-    Rows rw;
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      const int tq = wave + NW * j;
-      int tok = tile_start + 8 * tq + t8;
-      tok = tok < se ? tok : se - 1;
-      const int pg = tok / p.block_size;
-      const long long page = btab[pg];
-      rw.r[j] = cache + (page * p.block_stride + (long long)(tok - pg * p.block_size) * G::D) * 2 +
-                (x ^ swz(t8, tq)) * 16;
-    }
-    return rw;
-  }
   // a tile's column groups cq8 < CQ-1 (values) go to vbuf, the last (rope) to rbuf
   static constexpr int CQ = G::CHUNKS / 8;
   template <int I, bool NT>
@@ -793,10 +773,7 @@ struct Stage1AB {
   template <bool NT>
   static __device__ __forceinline__ void issue(const DecodeParams& p, int sa, int t, int se, int pg0, char* smem,
                                                const int* s_table, int hg) {
-    issue_rows<NT>(TL::rows(p, sa + kTile * t, se, pg0, s_table, hg), t, smem, hg);
-  }
-  template <bool NT>
-  static __device__ __forceinline__ void issue_rows(const typename TL::Rows& rw, int t, char* smem, int hg) {
+    const typename TL::Rows rw = TL::rows(p, sa + kTile * t, se, pg0, s_table, hg);
     char* vb = vslot(smem, t);
     char* rb = rslot(smem, t);
     static_for<LPW>([&](auto i) { TL::template issue<decltype(i)::value, NT>(rw, vb, rb, hg); });
@@ -959,51 +936,19 @@ struct Stage1AB {
     constexpr int NACC = QKW ? CA : CBB;
     constexpr int CB0 = QKW ? 0 : CA;              // first column block this wave accumulates
 
-    const int bs = p.block_size;
-    const int32_t* btab = p.block_table + (long long)b * p.bt_stride;
-    // end of the block-table window (the entries staged in LDS) starting at token s0
-    auto window_end = [&](int s0) {
-      const long long win_end = (long long)(s0 / bs + TABLE) * bs;
-      return win_end < e ? s0 + (int)((win_end - s0) / kTile) * kTile : e;
-    };
-
-    // The first window's prologue overlaps its three round trips: while the
-    // QK waves load Q, the PV waves stage the window's block-table entries and
-    // issue the first two tiles with page numbers read from the table in
-    // global memory.
-    __syncthreads();   // the previous piece's readers of s_table, s_flags, s_inv and the ring are done
     // Q^T operand (QK wave): lane = head r16 of block nb, dims 32ks + 8g .. +8
     bf16x8_t qf[2][G::KS];
-    {
-      const int se = window_end(a);
-      if constexpr (QKW) {
-        const int lane = threadIdx.x & 63;
-        const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + (long long)b * p.q_sb;
+    if constexpr (QKW) {
+      const int lane = threadIdx.x & 63;
+      const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + (long long)b * p.q_sb;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int h = hb + 16 * nb + (lane & 15);
+      for (int nb = 0; nb < 2; ++nb) {
+        const int h = hb + 16 * nb + (lane & 15);
 #pragma unroll
-          for (int ks = 0; ks < G::KS; ++ks)
-            qf[nb][ks] = *reinterpret_cast<const bf16x8_t*>(qb + (long long)h * p.q_sh + 32 * ks + 8 * (lane >> 4));
-        }
-      } else {
-        const int T = (se - a + kTile - 1) / kTile;
-        const int pg0 = a / bs;
-        const typename TL::Rows r0 = TL::rows_global(p, a, se, btab, hg);
-        typename TL::Rows r1 = r0;
-        if (T > 1) r1 = TL::rows_global(p, a + kTile, se, btab, hg);
-        const int npg = (se - 1) / bs - pg0 + 1;
-        for (int i = (int)threadIdx.x - 4 * 64; i < npg; i += 4 * 64) s_table[i] = btab[pg0 + i];
-        wait_vmcnt<0>();   // no load of this wave in flight when the tile loads start (see below)
-        issue_rows<NT>(r0, 0, smem, hg);
-        if (T > 1) issue_rows<NT>(r1, 1, smem, hg);
+        for (int ks = 0; ks < G::KS; ++ks)
+          qf[nb][ks] = *reinterpret_cast<const bf16x8_t*>(qb + (long long)h * p.q_sh + 32 * ks + 8 * (lane >> 4));
       }
-      if (threadIdx.x == 0) {
-        s_flags[0] = 0;
-        s_flags[1] = 0;
-      }
-      if constexpr (QKW) wait_vmcnt<0>();
-      __syncthreads();   // Q loaded, the table window staged, the flags clear
+      wait_vmcnt<0>();
     }
 
     f32x4_t acc[NACC][2];
@@ -1023,37 +968,38 @@ struct Stage1AB {
     };
     reset();
 
+    const int bs = p.block_size;
+    const int32_t* btab = p.block_table + (long long)b * p.bt_stride;
     // One block-table window at a time.  Softmax reference: each head's is
     // fixed by its first tile of the pass and p = 2^(s - m_ref) is summed
     // unscaled; a later tile more than kSlack above it makes every wave zero
     // its state and rewind to a with the larger reference (each redo raises
     // a reference by more than kSlack, so this ends).
-    bool staged = true;   // the first window's table, flags and first two tiles are in place
 #pragma unroll 1
     for (int sa = a; sa < e;) {
       const int pg0 = sa / bs;
-      const int se = window_end(sa);
-      const int T = (se - sa + kTile - 1) / kTile;
-      if (!staged) {
-        __syncthreads();   // earlier readers of s_table, s_flags and the ring are done
-        const int npg = (se - 1) / bs - pg0 + 1;
-        for (int i = threadIdx.x; i < npg; i += NW_ * 64) s_table[i] = btab[pg0 + i];
-        if (threadIdx.x == 0) {
-          s_flags[0] = 0;
-          s_flags[1] = 0;
-        }
-        __syncthreads();
-        // No load of this wave is in flight here.  Saying so to the compiler
-        // (it does not see the tile loads, which are inline asm) keeps it from
-        // guarding registers that an earlier load wrote with a full vmcnt wait
-        // inside the tile loop, which would also drain the tile loads.
-        wait_vmcnt<0>();
-        if constexpr (!QKW) {
-          issue<NT>(p, sa, 0, se, pg0, smem, s_table, hg);
-          if (T > 1) issue<NT>(p, sa, 1, se, pg0, smem, s_table, hg);
-        }
+      const long long win_end = (long long)(pg0 + TABLE) * bs;
+      int se = e;
+      if (win_end < e) se = sa + (int)((win_end - sa) / kTile) * kTile;
+      __syncthreads();   // earlier readers of s_table, s_flags and the ring are done
+      const int npg = (se - 1) / bs - pg0 + 1;
+      for (int i = threadIdx.x; i < npg; i += NW_ * 64) s_table[i] = btab[pg0 + i];
+      if (threadIdx.x == 0) {
+        s_flags[0] = 0;
+        s_flags[1] = 0;
       }
-      staged = false;
+      __syncthreads();
+
+      const int T = (se - sa + kTile - 1) / kTile;
+      // No load of this wave is in flight here.  Saying so to the compiler
+      // (it does not see the tile loads, which are inline asm) keeps it from
+      // guarding registers that an earlier load wrote with a full vmcnt wait
+      // inside the tile loop, which would also drain the tile loads.
+      wait_vmcnt<0>();
+      if constexpr (!QKW) {
+        issue<NT>(p, sa, 0, se, pg0, smem, s_table, hg);
+        if (T > 1) issue<NT>(p, sa, 1, se, pg0, smem, s_table, hg);
+      }
       bool redo = false;
 #pragma unroll 1
       for (int k = 0; k <= T; ++k) {
