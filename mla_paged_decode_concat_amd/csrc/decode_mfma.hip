@@ -132,6 +132,14 @@ __device__ __forceinline__ int lane_now() {
   return l;
 }
 
+// The workgroup thread index formed the same way (wave index in a scalar
+// register, lane through lane_now()), for the strided loops that stage the
+// block table or clear an empty request's output: their per-thread addresses
+// are then formed where the loop runs instead of at kernel entry.
+__device__ __forceinline__ int tid_now() {
+  return (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * kWave + lane_now();
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(size_t)MLA_LDS(const char, p);
 }
@@ -433,7 +441,7 @@ struct Stage1 {
         if (win_end < e) se = sa + (int)((win_end - sa) / kTile) * kTile;
         __syncthreads();   // earlier readers of s_table, s_flags and the tile buffers are done
         const int npg = (se - 1) / bs - pg0 + 1;
-        for (int i = threadIdx.x; i < npg; i += NW * 64) s_table[i] = btab[pg0 + i];
+        for (int i = tid_now(); i < npg; i += NW * 64) s_table[i] = btab[pg0 + i];
         if (threadIdx.x == 0) {
           s_flags[0] = 0;
           s_flags[1] = 0;
@@ -939,7 +947,7 @@ struct Stage1AB {
     // Q^T operand (QK wave): lane = head r16 of block nb, dims 32ks + 8g .. +8
     bf16x8_t qf[2][G::KS];
     if constexpr (QKW) {
-      const int lane = threadIdx.x & 63;
+      const int lane = lane_now();   // Q's per-lane address terms formed here, per piece
       const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + (long long)b * p.q_sb;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
@@ -983,7 +991,7 @@ struct Stage1AB {
       if (win_end < e) se = sa + (int)((win_end - sa) / kTile) * kTile;
       __syncthreads();   // earlier readers of s_table, s_flags and the ring are done
       const int npg = (se - 1) / bs - pg0 + 1;
-      for (int i = threadIdx.x; i < npg; i += NW_ * 64) s_table[i] = btab[pg0 + i];
+      for (int i = tid_now(); i < npg; i += NW_ * 64) s_table[i] = btab[pg0 + i];
       if (threadIdx.x == 0) {
         s_flags[0] = 0;
         s_flags[1] = 0;
@@ -1342,7 +1350,7 @@ struct Stage1AB8 {
     // half ks % 2 in k-step ks
     bf16x8_t qf[2][G::KS];
     if constexpr (QKW) {
-      const int lane = threadIdx.x & 63;
+      const int lane = lane_now();   // Q's per-lane address terms formed here, per piece
       const int g = lane >> 4;
       const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + (long long)b * p.q_sb;
 #pragma unroll
@@ -1383,7 +1391,7 @@ struct Stage1AB8 {
       if (win_end < e) se = sa + (int)((win_end - sa) / kTile) * kTile;
       __syncthreads();
       const int npg = (se - 1) / bs - pg0 + 1;
-      for (int i = threadIdx.x; i < npg; i += NW_ * 64) s_table[i] = btab[pg0 + i];
+      for (int i = tid_now(); i < npg; i += NW_ * 64) s_table[i] = btab[pg0 + i];
       if (threadIdx.x == 0) {
         s_flags[0] = 0;
         s_flags[1] = 0;
@@ -1568,7 +1576,7 @@ struct Stage1TS {
       if (win_end < e) se = sa + (int)((win_end - sa) / kTile) * kTile;
       __syncthreads();   // every wave is done with the previous window's table and its slot
       const int npg = (se - 1) / bs - pg0 + 1;
-      for (int i = threadIdx.x; i < npg; i += 4 * 64) s_table[i] = btab[pg0 + i];
+      for (int i = tid_now(); i < npg; i += 4 * 64) s_table[i] = btab[pg0 + i];
       __syncthreads();
       const int ntiles = (se - sa + kTile - 1) / kTile;
 #pragma unroll 1
@@ -1812,8 +1820,8 @@ __global__ __launch_bounds__(K::NW_ * 64) void stage1_mfma_kernel(DecodeParams p
         // here when there is no stage 2 to write them
         constexpr int R = K::G::D - 64;
         uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.o) + ((long long)b * p.H + head0) * R);
-        for (int i = threadIdx.x; i < K::HPG * R / 8; i += K::NW_ * 64) o[i] = make_uint4(0, 0, 0, 0);
-        for (int i = threadIdx.x; i < K::HPG; i += K::NW_ * 64) p.lse[(long long)b * p.H + head0 + i] = -INFINITY;
+        for (int i = tid_now(); i < K::HPG * R / 8; i += K::NW_ * 64) o[i] = make_uint4(0, 0, 0, 0);
+        for (int i = tid_now(); i < K::HPG; i += K::NW_ * 64) p.lse[(long long)b * p.H + head0 + i] = -INFINITY;
       }
       if (n <= 0 || e <= a || n < p.len_min || n >= p.len_max) break;
     } else {
