@@ -350,8 +350,8 @@ struct Stage1 {
   template <bool NT>
   static __device__ void piece(const DecodeParams& p, int b, int a, int e, int part, int head0,
                                char* smem, int* s_table, int* s_flags) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int lane = lane_now();   // per-lane terms formed per piece, not at kernel entry
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4;
     const int r16 = lane & 15;
     head0 += wave * 16 * NB;                   // this wave's heads
@@ -1513,8 +1513,8 @@ struct Stage1TS {
   template <bool NT>
   static __device__ void piece(const DecodeParams& p, int b, int a, int e, int part, int head0,
                                char* smem, int* s_table, int* s_flags) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int lane = lane_now();   // per-lane terms formed per piece, not at kernel entry
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4;
     const int r16 = lane & 15;
 
