@@ -129,6 +129,10 @@ def parse():
                     help="run only the warmup and timed step loop (profiler runs: every decode launch is a step's)")
     ap.add_argument("--num-kv-splits", type=int, default=0,
                     help="splits per request in the step loop (0 = the library's rule; 1 = the batch-invariant step)")
+    ap.add_argument("--data", choices=["workload", "zeros", "ones"], default="workload",
+                    help="contents of the cache and queries in the step loop: the workload's N(0,1) values "
+                         "(default), or all 0.0 / all 1.0 after the bulk write (a check of how the stage-1 "
+                         "time depends on the data the matrix cores see; not the benchmark)")
     ap.add_argument("--configs-only", action="store_true",
                     help="run only the per-workload runs (profiler runs: one bulk cache write opens each workload)")
     return ap.parse_args()
@@ -193,6 +197,11 @@ def main():
     step_kv_c = bt.kv_c.index_select(0, idx).contiguous()
     step_k_pe = bt.k_pe.index_select(0, idx).contiguous()
     step_slots = bt.slot_mapping.index_select(0, idx).contiguous()
+    if args.data != "workload":
+        # constant contents: the same work and bytes, no bit toggling in the data paths
+        val = 0.0 if args.data == "zeros" else 1.0
+        for t in (bt.cache, bt.q, step_kv_c, step_k_pe):
+            t.fill_(val)
     ws = torch.empty(M.decode_workspace_bytes(B, H, S, R) // 4, dtype=torch.float32, device=dev)
     o = torch.empty((B, H, R), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, H), dtype=torch.float32, device=dev)
@@ -367,7 +376,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
+        "data": "synthetic" if args.data == "workload" else f"synthetic, cache and q all {args.data} (data check)",
         "config": {
             "workload": "DeepSeek-V3 per-GPU MLA decode, bf16: B=64, H=128, seq_len 8192 each, kv_lora_rank 512, "
                         "rope_dim 64, block_size 64, random block table, N(0,1) inputs, sm_scale 1/sqrt(192); "
