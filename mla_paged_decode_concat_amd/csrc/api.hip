@@ -344,7 +344,7 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
   } else {
     // as many MFMA workgroups per compute unit as fit at once (one for the
     // 64- and 128-head shapes, whose tile ring fills the LDS; two or three of
-    // the one-wave shapes); the vector kernel runs four per CU
+    // the one-wave shapes); the vector kernel's grid is four workgroups per CU
     const int per_cu =
         use_mfma ? mfma_wgs_per_cu(p.heads_per_group, kv_lora_rank, cache_dtype, device_lds_per_cu()) : 4;
     int g = cus * per_cu / groups;
@@ -366,10 +366,10 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
   // XCD and still finds the lines); tiles shared by more groups are meant to
   // meet in L2
   p.kv_nt = groups <= 2 ? 1 : 0;
-  // one partial per request: the matrix-core stage 1 writes o and lse
-  // itself (the merge of a single partial is the identity, bit for bit), so
-  // there is no stage 2 and no workspace traffic
-  p.direct = use_mfma && num_kv_splits == 1 ? 1 : 0;
+  // one partial per request: stage 1 writes o and lse itself (the merge of a
+  // single partial is the identity, bit for bit), so there is no stage 2 and
+  // no workspace traffic
+  p.direct = num_kv_splits == 1 ? 1 : 0;
   hipError_t e;
   if (split_len > 0) {
     DecodeParams pt = p;

@@ -6,16 +6,19 @@
 // _fwd_grouped_kernel_stage1): scores over the full R + P row, values = the
 // first R columns of the same row, online softmax, store acc / l and m + ln l.
 //
-// Layout: 4 waves per workgroup; wave w takes every 4th token of the partial.
+// Layout: 8 waves per workgroup; wave w takes every 8th token of the partial
+// (a token's dot products, online-softmax step and output update form a
+// dependent chain, so more waves per partial shorten it: the tiny fp32
+// workload's stage 1 took 21 us with 8, 32 us with 4 and 20-31 us with 16).
 // A lane holds columns lane + 64 j of the current row, so each row read is
 // coalesced; per-token dot products are finished with a wave butterfly.  The
-// four waves' (max, sum, acc) are merged through LDS at the end.
+// waves' (max, sum, acc) are merged through LDS at the end.
 #include "mla_device.h"
 #include "mla_launch.h"
 
 namespace mla {
 
-constexpr int kValuWaves = 4;
+constexpr int kValuWaves = 8;
 constexpr int kValuHeads = 4;   // heads per workgroup
 
 template <int CT>
@@ -115,8 +118,19 @@ __device__ void valu_piece(const DecodeParams& p, int b, int h0, int a, int e, i
       o += sm_acc[w][hh][d] * c;
     }
     if (h < p.H) {
-      ws_row(p, part, h, R)[d] = o / L * kvs;
-      if (d == 0) *ws_lse(p, part, h, R) = M + logf(L);
+      const float v = o / L * kvs;
+      if (p.direct) {
+        // one partial per request: o and lse themselves, the same bits as
+        // the merge of the single partial (weight exp(0) = 1, sum 1; its
+        // fused 1 * v + 0 turns a -0 into +0, as the + 0.0f here does)
+        const long long bh = (long long)b * p.H + h;
+        if constexpr (QT == DT_F32) reinterpret_cast<float*>(p.o)[bh * R + d] = v + 0.0f;
+        else reinterpret_cast<uint16_t*>(p.o)[bh * R + d] = (uint16_t)f32_to_bf16_rne(v + 0.0f);
+        if (d == 0) p.lse[bh] = M + logf(L);
+      } else {
+        ws_row(p, part, h, R)[d] = v;
+        if (d == 0) *ws_lse(p, part, h, R) = M + logf(L);
+      }
     }
   }
   __syncthreads();   // LDS is reused by the next piece
@@ -133,7 +147,19 @@ __global__ __launch_bounds__(kWave * kValuWaves) void stage1_valu_kernel(DecodeP
     const int b = blockIdx.x / p.S;
     const int s = blockIdx.x - b * p.S;
     const int n = p.seq_lens[b];
-    if (n <= 0) return;
+    if (n <= 0) {
+      if (p.direct) {   // an empty request: o = 0, lse = -inf, as the merge would write
+        for (int i = threadIdx.x; i < kValuHeads * R; i += kWave * kValuWaves) {
+          const int h = h0 + i / R;
+          if (h >= p.H) continue;
+          const long long idx = ((long long)b * p.H + h) * R + i % R;
+          if constexpr (QT == DT_F32) reinterpret_cast<float*>(p.o)[idx] = 0.0f;
+          else reinterpret_cast<uint16_t*>(p.o)[idx] = 0;
+          if (i % R == 0) p.lse[(long long)b * p.H + h] = -INFINITY;
+        }
+      }
+      return;
+    }
     int a, e;
     literal_piece_range(n, p.S, p.piece_len, s, a, e);
     if (e <= a) return;

@@ -232,7 +232,7 @@ struct DecodeParams {
   int token_split;                 // stage 1, 16- or 32-head groups: four waves split the tokens
   int kv_nt;                       // stage-1 tile loads carry the non-temporal hint (<= 2 head groups)
   int direct;                      // one partial per request (num_kv_splits == 1): stage 1 writes o
-                                   // (bf16) and lse itself and stage 2 is not launched
+                                   // (q's dtype) and lse itself and stage 2 is not launched
   int len_min, len_max;            // literal partition: this stage-1 launch takes the requests
                                    // with len_min <= seq_len < len_max
   int piece_len;                   // literal partition: tokens per piece (0 = ceil(n / S))
