@@ -277,6 +277,7 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
   p.H = H;
   p.S = num_kv_splits;
   p.block_size = block_size;
+  p.bs_log2 = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
   if (num_kv_splits == 1 || op.partition == 1 || op.partition == 3) p.partition = PART_LITERAL;
   else p.partition = PART_BALANCED;
   p.piece_len = op.piece_len;

@@ -199,10 +199,10 @@ struct TileLoad {
       const int tq = wave + NW * j;
       int tok = tile_start + 8 * tq + t8;
       tok = tok < se ? tok : se - 1;              // past the range: re-read a valid row (masked later)
-      const int pg = tok / p.block_size;
+      int pg, row;
+      page_split(p, tok, pg, row);
       const long long page = s_table[pg - pg0];
-      rw.r[j] = cache + (page * p.block_stride + (long long)(tok - pg * p.block_size) * G::D) * 2 +
-                (x ^ swz(t8, tq)) * 16;
+      rw.r[j] = cache + (page * p.block_stride + (long long)row * G::D) * 2 + (x ^ swz(t8, tq)) * 16;
     }
     return rw;
   }
@@ -254,9 +254,10 @@ struct TileLoad8 {
   static __device__ __forceinline__ const char* row_ptr(const DecodeParams& p, int tok, int se, int pg0,
                                                         const int* s_table) {
     tok = tok < se ? tok : se - 1;                 // past the range: re-read a valid row (masked later)
-    const int pg = tok / p.block_size;
+    int pg, row;
+    page_split(p, tok, pg, row);
     const long long page = s_table[pg - pg0];
-    return reinterpret_cast<const char*>(p.cache) + page * p.block_stride + (long long)(tok - pg * p.block_size) * D;
+    return reinterpret_cast<const char*>(p.cache) + page * p.block_stride + (long long)row * D;
   }
   static __device__ __forceinline__ Rows rows(const DecodeParams& p, int tile_start, int se, int pg0,
                                               const int* s_table, int wave) {

@@ -226,6 +226,7 @@ struct DecodeParams {
   float sm_scale;
   int B, H, S;
   int block_size;
+  int bs_log2;                     // log2(block_size) when it is a power of two, else -1
   int partition;                   // PART_LITERAL | PART_BALANCED
   int G;                           // balanced: chunk count
   int heads_per_group;             // stage 1: heads per workgroup
@@ -242,6 +243,18 @@ struct DecodeParams {
 // pages): the normalised partial outputs as rows [H, B*S, R] -- each row a
 // multiple of 1 KB, so rows start on cache lines, and the slots of one head
 // are consecutive rows -- followed by their LSEs [H, B*S].
+// Page of token tok (tok >= 0) and its row in that page: a shift and a mask
+// for the usual power-of-two block sizes (the branch is uniform), else the
+// integer division, which costs a few dozen vector instructions per use.
+__device__ __forceinline__ void page_split(const DecodeParams& p, int tok, int& pg, int& row) {
+  if (p.bs_log2 >= 0) {
+    pg = tok >> p.bs_log2;
+    row = tok & (p.block_size - 1);
+  } else {
+    pg = tok / p.block_size;
+    row = tok - pg * p.block_size;
+  }
+}
 __device__ __forceinline__ float* ws_row(const DecodeParams& p, int slot, int h, int R) {
   return p.ws + ((long long)h * p.B * p.S + slot) * R;
 }
