@@ -119,12 +119,12 @@ def test_late_dominant_token_forces_redo(index):
             compare(o, lse, o_ref, lse_ref, bt.spec.in_dtype)
 
 
-@pytest.mark.parametrize("bs", [1, 16, 48, 64])
+@pytest.mark.parametrize("bs,H", [(1, 32), (16, 32), (48, 32), (64, 32), (16, 128), (48, 128)])
 @pytest.mark.parametrize("index", [1, 4])
-def test_block_sizes(bs, index):
+def test_block_sizes(bs, H, index):
     spec = W.SPECS[index]
     lens = [1, 31, 33, 1500, 2049]
-    bt = W.make_batch(index, DEV, seq_lens=lens, H=32)
+    bt = W.make_batch(index, DEV, seq_lens=lens, H=H)
     # rebuild the paging with block size bs over the same token rows
     nblk = [-(-n // bs) for n in lens]
     g = torch.Generator().manual_seed(bs)
@@ -151,8 +151,13 @@ def test_block_sizes(bs, index):
     assert np.array_equal(W.bits(bt.cache), ref_cache)
     o_ref, lse_ref = oracle_decode(bt, ref_cache, SM)
     # the token-split kernels (bf16 cache only) with 16- and 32-head groups;
-    # block size 1 stages the table of a 2049-token request in three windows
-    runs = [(1, 0), (2, 0)] + ([(3, 16), (3, 32)] if spec.cache_dtype == "bf16" else [])
+    # block size 1 stages the table of a 2049-token request in three windows.
+    # At 128 heads: the two-role kernels (128-head groups), whose tile
+    # addresses take the division path for block size 48 and the shift for 16
+    if H == 128:
+        runs = [(2, 128)]
+    else:
+        runs = [(1, 0), (2, 0)] + ([(3, 16), (3, 32)] if spec.cache_dtype == "bf16" else [])
     for S in [1, 4]:
         for kernel, hpg in runs:
             for partition in [1, 2]:
