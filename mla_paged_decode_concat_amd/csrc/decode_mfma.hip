@@ -383,7 +383,9 @@ struct Stage1 {
     // l_sum: the exact sum of p (for the LSE); l_mma: the sum of p as rounded
     // to bf16 for the matrix cores, which normalises acc.  The normalised
     // weights then sum to one exactly, so the rounding of a dominant weight
-    // cancels instead of scaling the output by up to 2^-9.
+    // cancels instead of scaling the output by up to 2^-9.  With an fp8 cache
+    // the matrix cores take p as bf16 plus its bf16 remainder, which together
+    // are within 2^-17 of p, so l_sum normalises acc as well.
     float m_ref[NB], l_sum[NB], l_mma[NB], m_init[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) m_init[nb] = -INFINITY;
@@ -622,15 +624,13 @@ struct Stage1 {
                 ls += pj;
                 pf[nb][4 * mb + i] = pb;
                 if constexpr (F8) {
-                  const __bf16 pr = (__bf16)(pj - (float)pb);
-                  pl[nb][4 * mb + i] = pr;
-                  lm += (float)pb + (float)pr;
+                  pl[nb][4 * mb + i] = (__bf16)(pj - (float)pb);
                 } else {
                   lm += (float)pb;
                 }
               }
             l_sum[nb] += ls;
-            l_mma[nb] += lm;
+            l_mma[nb] += F8 ? ls : lm;
           }
 
           // ---- O^T += V^T P^T  (CB column blocks x NB head blocks); V^T read
@@ -1280,21 +1280,26 @@ struct Stage1AB8 {
     __builtin_amdgcn_s_setprio(0);
     bool need = false;
     float mt[2];
-    const bool full = tile_start + kTile <= se;
+    // scores scaled to the log2 domain; in a range's last tile the tokens
+    // past it score -inf (a uniform branch: full tiles skip the masks)
+    auto scale = [&](auto masked) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      mt[nb] = -INFINITY;
+      for (int nb = 0; nb < 2; ++nb) {
+        mt[nb] = -INFINITY;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = tile_start + 16 * mb + 4 * g + i;
-          const float v = full || tok < se ? s[mb][nb][i] * c2 : -INFINITY;
-          s[mb][nb][i] = v;
-          mt[nb] = fmaxf(mt[nb], v);
-        }
-      need |= mt[nb] > m_ref[nb] + kSlack;
-    }
+          for (int i = 0; i < 4; ++i) {
+            const int tok = tile_start + 16 * mb + 4 * g + i;
+            const float v = !decltype(masked)::value || tok < se ? s[mb][nb][i] * c2 : -INFINITY;
+            s[mb][nb][i] = v;
+            mt[nb] = fmaxf(mt[nb], v);
+          }
+        need |= mt[nb] > m_ref[nb] + kSlack;
+      }
+    };
+    if (tile_start + kTile <= se) scale(std::false_type{});
+    else scale(std::true_type{});
     if (__builtin_expect(__any(need), 0)) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
@@ -1314,21 +1319,20 @@ struct Stage1AB8 {
     bf16x8_t pf[2], pl[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      float ls = 0.0f, lm = 0.0f;
+      float ls = 0.0f;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float pj = __builtin_amdgcn_exp2f(s[mb][nb][i] - m_ref[nb]);
           const __bf16 pb = (__bf16)pj;
-          const __bf16 pr = (__bf16)(pj - (float)pb);
           ls += pj;
           pf[nb][4 * mb + i] = pb;
-          pl[nb][4 * mb + i] = pr;
-          lm += (float)pb + (float)pr;
+          pl[nb][4 * mb + i] = (__bf16)(pj - (float)pb);
         }
+      // P + remainder is within 2^-17 of p: the exact sum normalises acc too
       l_sum[nb] += ls;
-      l_mma[nb] += lm;
+      l_mma[nb] += ls;
     }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
