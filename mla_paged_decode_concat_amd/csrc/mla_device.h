@@ -239,10 +239,6 @@ struct DecodeParams {
   int piece_len;                   // literal partition: tokens per piece (0 = ceil(n / S))
 };
 
-// Workspace layout (fp32, B*H*S*(R+1) values as the split workspace of the
-// pages): the normalised partial outputs as rows [H, B*S, R] -- each row a
-// multiple of 1 KB, so rows start on cache lines, and the slots of one head
-// are consecutive rows -- followed by their LSEs [H, B*S].
 // Page of token tok (tok >= 0) and its row in that page: a shift and a mask
 // for the usual power-of-two block sizes (the branch is uniform), else the
 // integer division, which costs a few dozen vector instructions per use.
@@ -255,6 +251,10 @@ __device__ __forceinline__ void page_split(const DecodeParams& p, int tok, int& 
     row = tok - pg * p.block_size;
   }
 }
+// Workspace layout (fp32, B*H*S*(R+1) values as the split workspace of the
+// pages): the normalised partial outputs as rows [H, B*S, R] -- each row a
+// multiple of 1 KB, so rows start on cache lines, and the slots of one head
+// are consecutive rows -- followed by their LSEs [H, B*S].
 __device__ __forceinline__ float* ws_row(const DecodeParams& p, int slot, int h, int R) {
   return p.ws + ((long long)h * p.B * p.S + slot) * R;
 }
