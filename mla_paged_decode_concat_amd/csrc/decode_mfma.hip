@@ -374,10 +374,8 @@ struct Stage1 {
         qf[nb][ks] = *reinterpret_cast<const bf16x8_t*>(qb + (long long)h * p.q_sh + d);
       }
     }
-    // Q has landed before the tile loop starts: without this the compiler
-    // guards each first use of Q inside the loop with a vmcnt wait, which
-    // would also drain the tile loads in flight on every iteration.
-    wait_vmcnt<0>();
+    // Q is waited for after the block table's first window is staged (its
+    // loads are in flight together with Q's), before the tile loop.
 
     f32x4_t acc[G::CB][NB];
     // l_sum: the exact sum of p (for the LSE); l_mma: the sum of p as rounded
@@ -449,6 +447,11 @@ struct Stage1 {
           s_flags[0] = 0;
           s_flags[1] = 0;
         }
+        // Q (loaded at the top of the piece) and the table have landed before
+        // the tile loop: without this the compiler guards each first use of Q
+        // inside the loop with a vmcnt wait, which would also drain the tile
+        // loads in flight on every iteration.
+        wait_vmcnt<0>();
         __syncthreads();
 
         const int ntiles = (se - sa + kTile - 1) / kTile;
@@ -1494,8 +1497,10 @@ struct Stage1AB8 {
 // partition has fewer items than CUs), a workgroup whose waves share each
 // tile would leave each busy CU with a single load stream.  Here four waves
 // share the range's heads: wave w streams tiles w, w+4, ... into its own LDS
-// slot (its own 32-token tile, loaded by its own 36 instructions and waited
-// on by itself alone), with its own Q copy, accumulators and softmax
+// slot (its own 32-token tile, loaded by its own instructions and waited on
+// by itself alone; the next tile is loaded into the slot group by group as
+// the current one's QK and PV finish reading each part, and QK waits for
+// each group just before reading it), with its own Q copy, accumulators and softmax
 // reference (set by its first tile; a later tile more than kSlack above it
 // makes the workgroup redo the range with the larger reference, as in the
 // shared-tile kernel, so the accumulators are never rescaled and stay in
@@ -1513,6 +1518,8 @@ struct Stage1TS {
   static constexpr int SMEM = 4 * SLOT;
   static constexpr int TABLE = kTableWindow;
   static constexpr int MERGE_STAT = 4 * 16 * R;     // floats: per-wave accumulators of 16 heads, then statistics
+  static constexpr int CQ = G::CHUNKS / 8;          // 1 KB column groups per token quarter: CQ-1 value groups, the rope
+  static_assert(TL::LPW == 4 * CQ, "one wave loads the whole tile, 4 token quarters per group");
   static_assert((MERGE_STAT + 4 * 3 * 16) * 4 <= SMEM, "merge area inside the tile slots");
 
   template <bool NT>
@@ -1531,7 +1538,7 @@ struct Stage1TS {
 #pragma unroll
       for (int ks = 0; ks < G::KS; ++ks) qf[nb][ks] = *reinterpret_cast<const bf16x8_t*>(qb + 32 * ks + 8 * g);
     }
-    wait_vmcnt<0>();
+    // Q is waited for after the window's block table is staged (in flight together)
 
     uint32_t k_off[2];
 #pragma unroll
@@ -1582,13 +1589,25 @@ struct Stage1TS {
       __syncthreads();   // every wave is done with the previous window's table and its slot
       const int npg = (se - 1) / bs - pg0 + 1;
       for (int i = tid_now(); i < npg; i += 4 * 64) s_table[i] = btab[pg0 + i];
+      // Q and the table have landed, and no load of this wave is in flight:
+      // the tile loop's waits below count this wave's tile loads alone
+      wait_vmcnt<0>();
       __syncthreads();
       const int ntiles = (se - sa + kTile - 1) / kTile;
+      char* rbuf = slot + (CQ - 1) * 4096;
 #pragma unroll 1
       for (int t = wave; t < ntiles; t += 4) {
         const int tile_start = sa + kTile * t;
-        TL::template tile<NT>(p, tile_start, se, pg0, slot, slot + (G::CHUNKS / 8 - 1) * 4096, s_table, 0, lane);
-        wait_vmcnt<0>();   // this wave's own tile; no other wave reads it
+        // A wave's first tile of the window is issued here; each later one was
+        // issued group by group while the previous tile's PV freed its slot.
+        // Either way the groups go out rope first, then value groups 0, 1, ...
+        // (4 loads each), so QK waits for the group it reads next alone.
+        if (t == wave) {
+          const typename TL::Rows rw = TL::rows(p, tile_start, se, pg0, s_table, 0);
+          static_for<TL::LPW>([&](auto i) {
+            TL::template issue<(decltype(i)::value + 4 * (CQ - 1)) % TL::LPW, NT>(rw, slot, rbuf, 0);
+          });
+        }
         const char* tile = slot;
 
         f32x4_t sc[2][NB];
@@ -1597,15 +1616,19 @@ struct Stage1TS {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) sc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         bf16x8_t kr[3][2];
+        wait_vmcnt<4 * (CQ - 2)>();   // the rope and value group 0 have landed
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
             kr[ks][mb] = *MLA_LDS(const bf16x8_t, tile + ((ks >> 1) * 4 + 2 * mb) * 1024 + k_off[ks & 1]);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ks = 0; ks < G::KS; ++ks) {
-          if (ks + 2 < G::KS) {
+        static_for<G::KS>([&](auto KSI) {
+          constexpr int ks = decltype(KSI)::value;
+          if constexpr (ks + 2 < G::KS) {
+            // value group (ks + 2) / 2 is read from here on: wait for its 4 loads
+            constexpr int gq = (ks + 2) >> 1;
+            if constexpr (((ks + 2) & 1) == 0 && gq < CQ - 1) wait_vmcnt<4 * (CQ - 2 - gq)>();
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
               kr[(ks + 2) % 3][mb] =
@@ -1617,6 +1640,16 @@ struct Stage1TS {
             for (int nb = 0; nb < NB; ++nb)
               sc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks % 3][mb], qf[nb][ks], sc[mb][nb], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
+        });
+
+        // The K reads are done (the matrix cores hold them): the rope part of
+        // the slot is free, and value group c is free once PV has read it.
+        // The wave's next tile goes into those parts as they free up.
+        const bool more = t + 4 < ntiles;
+        typename TL::Rows nrw;
+        if (more) {
+          nrw = TL::rows(p, tile_start + 4 * kTile, se, pg0, s_table, 0);
+          static_for<4>([&](auto i) { TL::template issue<4 * (CQ - 1) + decltype(i)::value, NT>(nrw, slot, rbuf, 0); });
         }
 
         // online softmax in the log2 domain; lane owns head 16nb + r16, tokens 16mb + 4g + i
@@ -1666,15 +1699,21 @@ struct Stage1TS {
         vr[0] = vread(0);
         vr[1] = vread(1);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int cb = 0; cb < G::CB; ++cb) {
-          if (cb + 2 < G::CB) vr[(cb + 2) % 3] = vread(cb + 2);
+        static_for<G::CB>([&](auto CBI) {
+          constexpr int cb = decltype(CBI)::value;
+          if constexpr (cb + 2 < G::CB) vr[(cb + 2) % 3] = vread(cb + 2);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
             acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[cb % 3], pf[nb], acc[cb][nb], 0, 0, 0);
+          if constexpr ((cb & 3) == 3) {
+            // the last read of value group cb / 4 is consumed: refill it
+            if (more)
+              static_for<4>([&](auto i) { TL::template issue<4 * (cb >> 2) + decltype(i)::value, NT>(nrw, slot, rbuf, 0); });
+          }
           __builtin_amdgcn_sched_barrier(0);
-        }
+        });
       }
+      wait_vmcnt<0>();   // (nothing is in flight: a window's last tile issues no successor)
       sa = se;
     }
     if (over) s_flags[pass & 1] = 1;
