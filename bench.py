@@ -115,6 +115,10 @@ def parse():
     # against 197 us a few hundred steps later)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--min-untimed-steps", type=int, default=100,
+                    help="untimed steps before the timed ones: the --warmup steps, topped up to this many "
+                         "(the board's clocks dip after the first few dispatches and settle over the next "
+                         "~100 steps; fewer time that transient, not the kernels)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="bound on the CPU oracle's timed work (0 = skip)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -223,7 +227,8 @@ def main():
         M.decode(bt.q, bt.cache, bt.block_table, bt.seq_lens, W.SM_SCALE, S_, R, workspace=ws, o=o, lse=lse,
                  stage_events=evs, **kw)
 
-    for _ in range(args.warmup):
+    untimed = max(args.warmup, args.min_untimed_steps)
+    for _ in range(untimed):
         step(S)
     torch.cuda.synchronize()
     K = args.steps
@@ -380,6 +385,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "untimed_steps": untimed,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": False,
         "scaling": "weak",
