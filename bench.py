@@ -36,16 +36,22 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 class HipEvent:
     """A raw HIP event (timing enabled).  The library records it on the
     stream it launches on; torch.cuda.Event cannot be used for that because
-    torch creates its event lazily on its own record()."""
+    torch creates its event lazily on its own record().  The events only
+    time work (they are read after a device synchronisation), so they skip
+    the system-scope fence a default event performs when it completes: that
+    fence writes back and invalidates the caches, which costs the step time
+    and adds to the interval the event measures."""
     _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
 
     def __init__(self):
         import ctypes
         if HipEvent._hip is None:
             HipEvent._hip = ctypes.CDLL("libamdhip64.so.7")
         self.handle = ctypes.c_void_p()
-        if HipEvent._hip.hipEventCreate(ctypes.byref(self.handle)) != 0:
-            raise RuntimeError("hipEventCreate failed")
+        if HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.handle),
+                                                 ctypes.c_uint(HipEvent.DISABLE_SYSTEM_FENCE)) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
 
     @property
     def cuda_event(self):
