@@ -302,10 +302,16 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
   // allows no group wider than 16, whatever the batch size: then every batch
   // runs it.  Measured against the one-wave kernel: 2.6x on batch-invariant
   // V2-Lite decode and 4-5% on 512 requests of 2048 tokens, 6% slower at
-  // 1024 x 700 tokens and 8.6 us slower at 300 x 100 tokens.  Balanced
-  // chunks are long or short depending on lengths the host does not see
-  // (16-19% faster for long ones, 7% slower for the V2-Lite mix), so there
-  // it is opt-in.
+  // 1024 x 700 tokens and 8.6 us slower at 300 x 100 tokens.  Under the
+  // balanced partition (no batch invariance to keep) it is the default for
+  // 16-head groups while the batch is below two requests per four-wave
+  // workgroup of the grid (one per CU and group): with the next tile
+  // refilling each wave's slot it is faster on every such shape measured
+  // (decode, H = 16: the V2-Lite mix 33.8 -> 33.1 us, 8 x 8192 44 -> 38,
+  // 32 x 1024 58 -> 38, 384 x 2048 178 -> 172; R = 256: 32 x 1024 47 -> 27,
+  // 512 x 2048 135 -> 126), while with more requests a chunk holds several
+  // of them and the per-range merge of the four waves costs more than the
+  // extra streams buy (R = 512: 512 x 2048 213 -> 219, 1024 x 700 176 -> 185).
   p.token_split = 0;
   p.len_min = 0;
   p.len_max = INT_MAX;
@@ -317,8 +323,9 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
     groups = H / p.heads_per_group;
     p.token_split = 1;
   } else if (use_mfma && p.heads_per_group == 16 && op.kernel == 0 && cache_dtype == MLA_BF16 && !op.grid &&
-             p.partition == PART_LITERAL) {
-    p.token_split = H % 32 != 0 ? 1 : 0;
+             H % 32 != 0) {
+    if (p.partition == PART_LITERAL) p.token_split = 1;
+    else p.token_split = (long long)B * groups < 2LL * cus ? 1 : 0;
   }
   // Batch-invariant decode (one partial per request) with a head count that
   // 32 divides: a long request is served by four waves that each stream a
