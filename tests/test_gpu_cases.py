@@ -449,3 +449,21 @@ def test_fixed_piece_partition_rejects_short_cover():
         _decode(bt, 1, partition=3, piece_len=max_len - 1)
     o, lse = _decode(bt, 1, partition=3, piece_len=max_len)     # one piece per request: fits
     assert torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("below", [True, False])
+def test_default_stage1_for_16_head_groups_under_balanced(below):
+    """H = 16, bf16 cache, num_kv_splits > 1 (balanced partition): the
+    default stage 1 is the 16-head token split while B * groups < 2 * CUs
+    and the one-wave shared-tile kernel from there on -- the same bits as
+    the explicit choice on either side of the threshold."""
+    cus = torch.cuda.get_device_properties(DEV).multi_processor_count
+    B = 2 * cus - 1 if below else 2 * cus
+    bt = W.make_batch(1, DEV, B=B, max_len=200)
+    _write(bt)
+    _print(f"[default16] B={B} cus={cus}")
+    o, lse = _decode(bt, 2)
+    oe, le = _decode(bt, 2, kernel=3 if below else 2)
+    assert torch.equal(o, oe) and torch.equal(lse, le)
+    other = _decode(bt, 2, kernel=2 if below else 3)
+    assert not torch.equal(o, other[0])      # the two kernels sum in different orders
