@@ -309,10 +309,13 @@ int mla_decode(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_dtyp
  *                3 = the MFMA stage 1 with four waves splitting each token
  *                range of a 16- or 32-head group (bf16 cache; 16 heads per
  *                group unless heads_per_group is 32).  The default takes 3
- *                for 16-head groups of a bf16 cache when H is not a
- *                multiple of 32 (with the default grid): always under the
- *                literal partitions, and under the balanced one while
- *                B * (H / 16) < 2 * compute units.
+ *                for a bf16 cache with the default grid: with 16-head
+ *                groups when H is not a multiple of 32 (always under the
+ *                literal partitions; under the balanced one while
+ *                B * (H / 16) < 2 * compute units), and with 32-head groups
+ *                for H = 32 or 64 at kv_lora_rank 512 under the balanced
+ *                partition while B * (H / 32) < 2 * compute units (and
+ *                heads_per_group is left at 0).
  *   grid       : balanced partition only: number of token chunks the batch
  *                is cut into (0 = derived from the compute-unit count).
  *   heads_per_group : heads handled by one stage-1 workgroup (0 = default).

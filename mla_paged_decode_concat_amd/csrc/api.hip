@@ -326,6 +326,18 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
              H % 32 != 0) {
     if (p.partition == PART_LITERAL) p.token_split = 1;
     else p.token_split = (long long)B * groups < 2LL * cus ? 1 : 0;
+  } else if (use_mfma && op.kernel == 0 && !op.heads_per_group && cache_dtype == MLA_BF16 && !op.grid &&
+             p.partition == PART_BALANCED && kv_lora_rank == 512 && (H == 32 || H == 64) &&
+             (long long)B * (H / 32) < 2LL * cus) {
+    // the same rule for 32 and 64 heads at R = 512, with 32-head groups
+    // (decode, default -> token split: H = 32, 64 x 8192 120.7 -> 111.0 us,
+    // 128 x 2048 89.0 -> 70.3, 256 x 2048 130.2 -> 118.1; H = 64, 16 x 8192
+    // 72.7 -> 57.6, 64 x 8192 154.2 -> 155.9; past the threshold, H = 32,
+    // 512 x 1024 137.7 -> 142.8).  At R = 256 the one-wave kernel keeps
+    // three workgroups per CU and stays ahead (H = 32: 60.0 against 66.5).
+    p.heads_per_group = 32;
+    groups = H / 32;
+    p.token_split = 1;
   }
   // Batch-invariant decode (one partial per request) with a head count that
   // 32 divides: a long request is served by four waves that each stream a

@@ -451,19 +451,24 @@ def test_fixed_piece_partition_rejects_short_cover():
     assert torch.isfinite(lse).all()
 
 
-@pytest.mark.parametrize("below", [True, False])
-def test_default_stage1_for_16_head_groups_under_balanced(below):
-    """H = 16, bf16 cache, num_kv_splits > 1 (balanced partition): the
-    default stage 1 is the 16-head token split while B * groups < 2 * CUs
-    and the one-wave shared-tile kernel from there on -- the same bits as
-    the explicit choice on either side of the threshold."""
+@pytest.mark.parametrize("index,H,below", [(1, 16, True), (1, 16, False), (3, 16, True), (2, 32, True),
+                                           (2, 32, False), (2, 64, True)])
+def test_default_stage1_for_small_head_counts_under_balanced(index, H, below):
+    """bf16 cache, num_kv_splits > 1 (balanced partition), 16 heads (any
+    rank) or 32 and 64 heads (R = 512): the default stage 1 is the token
+    split (16- or 32-head groups) while B * groups < 2 * CUs and the
+    shared-tile kernel from there on -- the same bits as the explicit choice
+    on either side of the threshold."""
     cus = torch.cuda.get_device_properties(DEV).multi_processor_count
-    B = 2 * cus - 1 if below else 2 * cus
-    bt = W.make_batch(1, DEV, B=B, max_len=200)
+    hpg = 16 if H % 32 else 32
+    groups = H // hpg
+    B = (2 * cus + groups - 1) // groups - 1 if below else (2 * cus + groups - 1) // groups
+    bt = W.make_batch(index, DEV, B=B, max_len=200, H=H)
     _write(bt)
-    _print(f"[default16] B={B} cus={cus}")
+    _print(f"[default-small-H] workload {index} H={H} B={B} cus={cus}")
     o, lse = _decode(bt, 2)
-    oe, le = _decode(bt, 2, kernel=3 if below else 2)
+    ts = dict(kernel=3, heads_per_group=hpg)
+    oe, le = _decode(bt, 2, **(ts if below else dict(kernel=2)))
     assert torch.equal(o, oe) and torch.equal(lse, le)
-    other = _decode(bt, 2, kernel=2 if below else 3)
+    other = _decode(bt, 2, **(dict(kernel=2) if below else ts))
     assert not torch.equal(o, other[0])      # the two kernels sum in different orders
