@@ -314,8 +314,11 @@ int mla_decode(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_dtyp
  *                literal partitions; under the balanced one while
  *                B * (H / 16) < 2 * compute units), and with 32-head groups
  *                for H = 32 or 64 at kv_lora_rank 512 under the balanced
- *                partition while B * (H / 32) < 2 * compute units (and
- *                heads_per_group is left at 0).
+ *                partition while B * (H / 32) < 2 * compute units, and
+ *                for H = 128 at kv_lora_rank 512 under the balanced
+ *                partition while 4 * B <= compute units and
+ *                B * max_blocks_per_seq * block_size <= 768 * compute units
+ *                (heads_per_group left at 0 in both).
  *   grid       : balanced partition only: number of token chunks the batch
  *                is cut into (0 = derived from the compute-unit count).
  *   heads_per_group : heads handled by one stage-1 workgroup (0 = default).

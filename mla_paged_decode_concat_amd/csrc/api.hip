@@ -338,6 +338,20 @@ int mla_decode_ex(const void* q, int64_t q_stride_b, int64_t q_stride_h, int q_d
     p.heads_per_group = 32;
     groups = H / 32;
     p.token_split = 1;
+  } else if (use_mfma && op.kernel == 0 && !op.heads_per_group && cache_dtype == MLA_BF16 && !op.grid &&
+             p.partition == PART_BALANCED && kv_lora_rank == 512 && H == 128 && (long long)B * 4 <= cus &&
+             (long long)B * max_blocks_per_seq * block_size <= 768LL * cus) {
+    // 128 heads: the four 32-head groups of a token-split chunk each read
+    // its tiles, so it only pays while the batch is small -- few requests
+    // (the two-role kernel's chunks are then capped by the B * (S - 1)
+    // partial slots and leave CUs idle) and a short context (bounded on the
+    // host by the block table's width).  Decode, two-role -> token split:
+    // 8 x 8192 76.2 -> 43.4 us, 4 x 32768 86.0 -> 64.1, 64 x 2048 86.2 ->
+    // 63.3, 24 x 8192 100.4 -> 92.6, 48 x 4096 101.1 -> 99.4; beyond the
+    // bounds 32 x 8192 99.2 -> 118.8 and 160 x 1024 92.6 -> 120.8.
+    p.heads_per_group = 32;
+    groups = 4;
+    p.token_split = 1;
   }
   // Batch-invariant decode (one partial per request) with a head count that
   // 32 divides: a long request is served by four waves that each stream a

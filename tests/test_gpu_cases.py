@@ -452,18 +452,23 @@ def test_fixed_piece_partition_rejects_short_cover():
 
 
 @pytest.mark.parametrize("index,H,below", [(1, 16, True), (1, 16, False), (3, 16, True), (2, 32, True),
-                                           (2, 32, False), (2, 64, True)])
+                                           (2, 32, False), (2, 64, True), (2, 128, True), (2, 128, False)])
 def test_default_stage1_for_small_head_counts_under_balanced(index, H, below):
     """bf16 cache, num_kv_splits > 1 (balanced partition), 16 heads (any
     rank) or 32 and 64 heads (R = 512): the default stage 1 is the token
-    split (16- or 32-head groups) while B * groups < 2 * CUs and the
-    shared-tile kernel from there on -- the same bits as the explicit choice
-    on either side of the threshold."""
+    split (16- or 32-head groups) while B * groups < 2 * CUs, and for 128
+    heads (R = 512) while 4 * B <= CUs and the table's width bounds the
+    batch's tokens by 768 per CU; the shared-tile kernels from there on --
+    the same bits as the explicit choice on either side of the threshold."""
     cus = torch.cuda.get_device_properties(DEV).multi_processor_count
     hpg = 16 if H % 32 else 32
     groups = H // hpg
-    B = (2 * cus + groups - 1) // groups - 1 if below else (2 * cus + groups - 1) // groups
+    if H == 128:
+        B = cus // 4 if below else cus // 4 + 1
+    else:
+        B = (2 * cus + groups - 1) // groups - 1 if below else (2 * cus + groups - 1) // groups
     bt = W.make_batch(index, DEV, B=B, max_len=200, H=H)
+    assert B * bt.block_table.shape[1] * bt.spec.block_size <= 768 * cus
     _write(bt)
     _print(f"[default-small-H] workload {index} H={H} B={B} cus={cus}")
     o, lse = _decode(bt, 2)
